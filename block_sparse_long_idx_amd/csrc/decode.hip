@@ -1,0 +1,200 @@
+// Decode: one new query per sequence, at the last cache row, so it sees the
+// whole cache and its local block is the last block.  Same Index Branch and
+// Main Branch as the prefill row ("MiniMax Sparse Attention" explainer,
+// section 02 and Figure 1 caption; the pages report a decode speed-up in
+// Figure 4 without a kernel design).  Layout Q-outer, split-K:
+//   (1) split scan of k_idx: every wavefront scores a run of blocks against
+//       the sequence's index query and max-pools them (HBM streaming);
+//   (2) exp-free Top-k over the pooled row (shared Top-k kernel);
+//   (3) one work-group per (sequence, group, selected block): exact softmax
+//       of the G heads over that block -> fp32 partial (O_s, lse_s);
+//   (4) merge of the k partials in ascending block order through their
+//       log-sum-exp.
+#include "common.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+// (1) Each lane owns one (token, group) pair of 16 consecutive tokens and
+// computes its full d_idx-long dot product; lanes of the same group then
+// max-reduce.  Requires H_kv | 64.  Only blocks before the local block.
+template <int D>
+__global__ __launch_bounds__(256) void decode_scan_kernel(const __bf16* __restrict__ q_idx,
+                                                          const __bf16* __restrict__ k_idx,
+                                                          int64_t N, int H_kv, int nblk,
+                                                          int blocks_per_wave,
+                                                          float* __restrict__ P, int64_t ldp) {
+  const int b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tpi = kWave / H_kv;          // tokens per iteration
+  const int tok = lane / H_kv, r = lane % H_kv;
+  float q[D];
+  const __bf16* qp = q_idx + ((int64_t)b * H_kv + r) * D;
+#pragma unroll
+  for (int v = 0; v < D / 8; ++v) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 8 * v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[8 * v + e] = bf2f(x[e]);
+  }
+  const __bf16* kseq = k_idx + (int64_t)b * N * H_kv * D;
+  const int nb_scan = nblk - 1;  // non-local blocks
+  const int blk0 = ((int)blockIdx.x * 4 + wave) * blocks_per_wave;
+  for (int blk = blk0; blk < min(nb_scan, blk0 + blocks_per_wave); ++blk) {
+    float m = -INFINITY;
+    for (int t0 = 0; t0 < kBlock; t0 += tpi) {
+      const int64_t j = (int64_t)blk * kBlock + t0 + tok;
+      const __bf16* kr = kseq + (j * H_kv + r) * D;
+      float s = 0.f;
+#pragma unroll
+      for (int v = 0; v < D / 8; ++v) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(kr + 8 * v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf(q[8 * v + e], bf2f(x[e]), s);
+      }
+      m = fmaxf(m, s);
+    }
+    for (int o = H_kv; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    if (lane < H_kv) P[((int64_t)b * H_kv + r) * ldp + blk] = m;
+  }
+}
+
+// (3) Partial attention of G heads over one selected block.
+template <int DH>
+__global__ __launch_bounds__(256) void decode_attn_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const int32_t* __restrict__ sel, int64_t N, int H_q, int H_kv, int k, float scale_log2,
+    float* __restrict__ Opart, float* __restrict__ lse_part) {
+  extern __shared__ float sm[];  // q [G][DH] fp32, s [G][128] fp32
+  const int s_id = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const int G = H_q / H_kv;
+  const int32_t blk = sel[((int64_t)b * H_kv + r) * k + s_id];
+  if (blk < 0) return;
+  float* qs = sm;
+  float* ss = sm + G * DH;
+  const int t = threadIdx.x;
+  for (int e = t; e < G * DH; e += 256)
+    qs[e] = bf2f(q[((int64_t)b * H_q + r * G) * DH + e]);
+  __syncthreads();
+  const int64_t key0 = (int64_t)blk * kBlock;
+  const __bf16* Kb = K + ((int64_t)b * N) * H_kv * DH;
+  const __bf16* Vb = V + ((int64_t)b * N) * H_kv * DH;
+  // scores: (head, key) pairs
+  for (int e = t; e < G * kBlock; e += 256) {
+    const int hh = e / kBlock, key = e % kBlock;
+    const int64_t j = key0 + key;
+    float s = -INFINITY;
+    if (j < N) {
+      const __bf16* kr = Kb + (j * H_kv + r) * DH;
+      const float* qr = qs + hh * DH;
+      s = 0.f;
+      for (int v = 0; v < DH / 8; ++v) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(kr + 8 * v);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s = fmaf(qr[8 * v + u], bf2f(x[u]), s);
+      }
+      s *= scale_log2;
+    }
+    ss[hh * kBlock + key] = s;
+  }
+  __syncthreads();
+  // softmax per head (one wave per head at a time), probabilities in place
+  const int wave = t >> 6, lane = t & 63;
+  for (int hh = wave; hh < G; hh += 4) {
+    float* row = ss + hh * kBlock;
+    const float a = row[lane], c = row[lane + 64];
+    const float m = wave_max_f32(fmaxf(a, c));
+    const float pa = exp2f(a - m), pc = exp2f(c - m);
+    const float l = wave_sum_f32(pa + pc);
+    row[lane] = pa / l;
+    row[lane + 64] = pc / l;
+    if (lane == 0)
+      lse_part[(((int64_t)b * H_q + r * G + hh) * k) + s_id] = (m + log2f(l)) * 0.69314718055994531f;
+  }
+  __syncthreads();
+  // O_s[h][d] = sum_key p[h][key] V[key][d]
+  for (int e = t; e < G * DH; e += 256) {
+    const int hh = e / DH, d = e % DH;
+    const float* p = ss + hh * kBlock;
+    float acc = 0.f;
+    for (int key = 0; key < kBlock; ++key) {
+      const int64_t j = key0 + key;
+      if (j < N) acc = fmaf(p[key], bf2f(Vb[(j * H_kv + r) * DH + d]), acc);
+    }
+    Opart[(((int64_t)b * H_q + r * G + hh) * k + s_id) * DH + d] = acc;
+  }
+}
+
+// (4) merge in ascending slot order.
+__global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ Opart,
+                                                           const float* __restrict__ lse_part,
+                                                           int H_q, int d_h, int k, int n_sel,
+                                                           float* __restrict__ O,
+                                                           float* __restrict__ lse) {
+  const int64_t bh = blockIdx.x;  // b * H_q + h
+  const float* ls = lse_part + bh * k;
+  float M = -INFINITY;
+  for (int s = 0; s < n_sel; ++s) M = fmaxf(M, ls[s]);
+  float den = 0.f;
+  for (int s = 0; s < n_sel; ++s) den += __expf(ls[s] - M);
+  for (int d = threadIdx.x; d < d_h; d += 256) {
+    float acc = 0.f;
+    for (int s = 0; s < n_sel; ++s)
+      acc += __expf(ls[s] - M) * Opart[(bh * k + s) * d_h + d];
+    O[bh * d_h + d] = acc / den;
+  }
+  if (lse && threadIdx.x == 0) lse[bh] = M + __logf(den);
+}
+
+hipError_t launch_decode_scan(const void* q_idx, const void* k_idx, int B, int64_t N, int H_kv,
+                              int d_idx, int nblk, float* P, int64_t ldp, hipStream_t stream) {
+  const int bpw = 8;
+  const int waves = (int)ceil_div(max(nblk - 1, 1), bpw);
+  dim3 grid((unsigned)ceil_div(waves, 4), B), block(256);
+  auto* qi = static_cast<const __bf16*>(q_idx);
+  auto* ki = static_cast<const __bf16*>(k_idx);
+  switch (d_idx) {
+    case 32:
+      decode_scan_kernel<32><<<grid, block, 0, stream>>>(qi, ki, N, H_kv, nblk, bpw, P, ldp);
+      break;
+    case 64:
+      decode_scan_kernel<64><<<grid, block, 0, stream>>>(qi, ki, N, H_kv, nblk, bpw, P, ldp);
+      break;
+    case 128:
+      decode_scan_kernel<128><<<grid, block, 0, stream>>>(qi, ki, N, H_kv, nblk, bpw, P, ldp);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_attn(const void* q, const void* K, const void* V, const int32_t* sel,
+                              int B, int64_t N, int H_q, int H_kv, int d_h, int k, float scale,
+                              float* Opart, float* lse_part, hipStream_t stream) {
+  const int G = H_q / H_kv;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  dim3 grid(k, H_kv, B), block(256);
+  const size_t lds = sizeof(float) * (size_t)G * (d_h + kBlock);
+  auto* qq = static_cast<const __bf16*>(q);
+  auto* kk = static_cast<const __bf16*>(K);
+  auto* vv = static_cast<const __bf16*>(V);
+  if (d_h == 128)
+    decode_attn_kernel<128><<<grid, block, lds, stream>>>(qq, kk, vv, sel, N, H_q, H_kv, k,
+                                                          scale_log2, Opart, lse_part);
+  else if (d_h == 64)
+    decode_attn_kernel<64><<<grid, block, lds, stream>>>(qq, kk, vv, sel, N, H_q, H_kv, k,
+                                                         scale_log2, Opart, lse_part);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const float* Opart, const float* lse_part, int B, int H_q,
+                               int d_h, int k, int n_sel, float* O, float* lse,
+                               hipStream_t stream) {
+  decode_merge_kernel<<<(unsigned)((int64_t)B * H_q), 256, 0, stream>>>(Opart, lse_part, H_q,
+                                                                         d_h, k, n_sel, O, lse);
+  return hipGetLastError();
+}
+
+}  // namespace msa

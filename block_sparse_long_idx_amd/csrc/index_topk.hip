@@ -1,0 +1,275 @@
+// Index Branch kernels: index-score GEMM with block max-pooling, and the
+// exp-free Top-k over pooled block scores.
+//
+// Method: "MiniMax Sparse Attention" explainer
+// (minimax-sparse-attention-danialwang.pages.dev), Figure 1 caption (index
+// score -> Block Max Pooling -> Top-k per query and GQA group, local block
+// forced) and section 05 part 1 (Top-k on raw scores, since softmax keeps
+// their order; per-lane register heaps merged across the lanes).
+#include "common.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+// ---------------------------------------------------------------------------
+// Score GEMM + block max-pool.
+//
+// Work-group = (group r, tile of 256 query positions); 4 waves x 64 queries.
+// The WG sweeps key blocks kb = 0 .. lb(last query)-1 in ascending order:
+// each block's 128 index keys are staged once in LDS (double-buffered) and
+// shared by the 4 waves.  A wave computes S^T = K_blk . Q^T with keys as
+// MFMA rows and its queries as columns, so every lane's 16 accumulators are
+// 16 keys of one query: the 128-key max is an in-lane max plus one swap
+// between the two lane halves.  Only blocks strictly before a query's local
+// block are ever consumed (the local block is forced, never ranked), and
+// those blocks are entirely in the past, so no causal mask is needed.
+//
+// Output P[r][q - q_start][kb] fp32, row pitch ldp (multiple of 4).  Entries
+// for kb >= lb(q) are unspecified.
+// The d_idx dimension is permuted identically on both operands: lane half h
+// covers d in [h*D/2, (h+1)*D/2), k-step s takes 8 of them.  A dot product
+// does not depend on the order of its terms, so the scores are unchanged.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  // XOR swizzle of the 16-byte chunk index inside a key row so that 8
+  // consecutive rows read at the same logical chunk hit distinct banks.
+  return D == 32 ? ((row >> 1) & 3) : (row & 7);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void index_pool_kernel(
+    const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx,
+    int64_t q_start, int64_t Nq, int H_kv, int ntiles, float* __restrict__ P,
+    int64_t ldp) {
+  constexpr int S = D / 16;   // MFMA k-steps
+  constexpr int CH = D / 8;   // 16-byte chunks per key row
+  constexpr int LOADS = 128 * CH / 256;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2][128 * D];
+
+  const int r = blockIdx.y;
+  const int tile = ntiles - 1 - (int)blockIdx.x;  // long rows first
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63;
+  const int h = lane >> 5, n = lane & 31;
+  const int64_t q_end = q_start + Nq;
+  const int64_t q0 = q_start + (int64_t)tile * 256;
+  const int64_t qw0 = q0 + wave * 64;
+  const int64_t q_last = min(q0 + 255, q_end - 1);
+  const int kb_end = (int)(q_last / kBlock);
+  const int kb_end_w = qw0 < q_end ? (int)(min(qw0 + 63, q_end - 1) / kBlock) : 0;
+
+  // Query operand (MFMA B: 16 d x 32 queries), two column groups.
+  bf16x8 qb[2][S];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int64_t q = qw0 + 32 * c + n;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      if (q < q_end)
+        qb[c][s] = *reinterpret_cast<const bf16x8*>(
+            q_idx + (q * H_kv + r) * D + (D / 2) * h + 8 * s);
+      else
+        qb[c][s] = bf16x8{};
+    }
+  }
+
+  auto gload = [&](int kb, bf16x8 (&regs)[LOADS]) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int id = t + 256 * u;
+      const int row = id / CH, c = id % CH;
+      regs[u] = *reinterpret_cast<const bf16x8*>(
+          k_idx + (((int64_t)kb * kBlock + row) * H_kv + r) * D + 8 * c);
+    }
+  };
+  auto lstore = [&](int buf, const bf16x8 (&regs)[LOADS]) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int id = t + 256 * u;
+      const int row = id / CH, c = id % CH;
+      *reinterpret_cast<bf16x8*>(&lds[buf][row * D + 8 * (c ^ kswz<D>(row))]) = regs[u];
+    }
+  };
+
+  // The lane owns one query for the output: half 0 -> column group 0.
+  const int64_t q_own = qw0 + 32 * h + n;
+  float* prow = P + ((int64_t)r * Nq + (q_own - q_start)) * ldp;
+  const bool own_ok = q_own < q_end;
+  float pend[4] = {0.f, 0.f, 0.f, 0.f};
+
+  bf16x8 nxt[LOADS];
+  if (kb_end > 0) {
+    gload(0, nxt);
+    lstore(0, nxt);
+  }
+  __syncthreads();
+
+  for (int kb = 0; kb < kb_end; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < kb_end) gload(kb + 1, nxt);
+    if (kb < kb_end_w) {
+      float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = 32 * g + n;
+        bf16x8 a[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+          a[s] = *reinterpret_cast<const bf16x8*>(
+              &lds[buf][row * D + 8 * (((D / 16) * h + s) ^ kswz<D>(row))]);
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          acc0 = mfma32(a[s], qb[0][s], acc0);
+          acc1 = mfma32(a[s], qb[1][s], acc1);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          m0 = fmaxf(m0, acc0[j]);
+          m1 = fmaxf(m1, acc1[j]);
+        }
+      }
+      m0 = fmaxf(m0, __shfl_xor(m0, 32, kWave));
+      m1 = fmaxf(m1, __shfl_xor(m1, 32, kWave));
+      pend[kb & 3] = h ? m1 : m0;
+      if (own_ok && ((kb & 3) == 3 || kb == kb_end_w - 1))
+        *reinterpret_cast<f32x4*>(prow + (kb & ~3)) =
+            f32x4{pend[0], pend[1], pend[2], pend[3]};
+    }
+    if (kb + 1 < kb_end) lstore(buf ^ 1, nxt);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_index_pool(const void* q_idx, const void* k_idx, int64_t q_start,
+                             int64_t Nq, int H_kv, int d_idx, float* P, int64_t ldp,
+                             hipStream_t stream) {
+  const int ntiles = (int)ceil_div(Nq, 256);
+  dim3 grid(ntiles, H_kv), block(256);
+  auto* qi = static_cast<const __bf16*>(q_idx);
+  auto* ki = static_cast<const __bf16*>(k_idx);
+  switch (d_idx) {
+    case 32:
+      index_pool_kernel<32><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, P, ldp);
+      break;
+    case 64:
+      index_pool_kernel<64><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, P, ldp);
+      break;
+    case 128:
+      index_pool_kernel<128><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, P, ldp);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Exp-free Top-k, one wavefront per (query, group) row of pooled scores.
+//
+// Candidates are the blocks b < lb strictly before the local block.  Each
+// candidate becomes a unique 64-bit key (order-preserving score bits, then
+// ~b so that on equal scores the lower block ranks higher).  Every lane
+// scans a strided slice of the row and keeps its best LM keys in a sorted
+// register list; the wave then pops the global best k-1 keys one at a time
+// (a cross-lane max per pop).  The local block is added and the k ids are
+// written in ascending order.
+// ---------------------------------------------------------------------------
+template <int LM>
+__device__ __forceinline__ void list_insert(uint64_t (&lst)[LM], uint64_t key) {
+#pragma unroll
+  for (int j = LM - 1; j > 0; --j) {
+    const uint64_t up = lst[j - 1];
+    lst[j] = key > up ? up : (key > lst[j] ? key : lst[j]);
+  }
+  lst[0] = key > lst[0] ? key : lst[0];
+}
+
+template <int LM>
+__device__ __forceinline__ void topk_row(const float* __restrict__ prow, int lb, int k,
+                                         int32_t* __restrict__ out, int lane) {
+  const int K1 = k - 1;
+  if (lb <= K1) {  // every visible block is selected
+    if (lane < k) out[lane] = lane <= lb ? lane : -1;
+    return;
+  }
+  uint64_t lst[LM];
+#pragma unroll
+  for (int j = 0; j < LM; ++j) lst[j] = 0;  // below every real key
+  for (int b = lane; b < lb; b += kWave) {
+    const uint64_t key = ((uint64_t)ord_f32(prow[b]) << 32) | (uint32_t)(~b);
+    if (key > lst[LM - 1]) list_insert<LM>(lst, key);
+  }
+  int mine = lb;  // lane K1 keeps the local block
+  for (int p = 0; p < K1; ++p) {
+    const uint64_t best = wave_max_u64(lst[0]);
+    if (lst[0] == best) {
+#pragma unroll
+      for (int j = 0; j < LM - 1; ++j) lst[j] = lst[j + 1];
+      lst[LM - 1] = 0;
+    }
+    if (lane == p) mine = (int)(~(uint32_t)best);
+  }
+  // ascending order: rank of each of the k ids among lanes 0..k-1
+  int rank = 0;
+  for (int j = 0; j < k; ++j) {
+    const int o = __shfl(mine, j, kWave);
+    rank += o < mine;
+  }
+  if (lane < k) out[rank] = mine;
+}
+
+// rows: prefill = H_kv * Nq rows of P[r][iq][*]; decode = B * H_kv rows of
+// P[b][r][*] whose local block is nblk_dec - 1.
+template <int LM>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ P, int64_t ldp,
+                                                   int64_t nrows, int64_t Nq, int H_kv,
+                                                   int64_t q_start, int nblk_dec, int k,
+                                                   int32_t* __restrict__ sel) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= nrows) return;
+  int lb;
+  int32_t* out;
+  if (nblk_dec > 0) {
+    lb = nblk_dec - 1;
+    out = sel + row * k;  // row = b * H_kv + r  ->  sel[b][r][:]
+  } else {
+    const int r = (int)(row / Nq);
+    const int64_t iq = row % Nq;
+    lb = (int)((q_start + iq) / kBlock);
+    out = sel + (iq * H_kv + r) * k;
+  }
+  topk_row<LM>(P + row * ldp, lb, k, out, lane);
+}
+
+static hipError_t launch_topk(const float* P, int64_t ldp, int64_t nrows, int64_t Nq,
+                              int H_kv, int64_t q_start, int nblk_dec, int k, int32_t* sel,
+                              hipStream_t stream) {
+  dim3 grid((unsigned)ceil_div(nrows, 4)), block(256);
+  if (k <= 8)
+    topk_kernel<7><<<grid, block, 0, stream>>>(P, ldp, nrows, Nq, H_kv, q_start, nblk_dec, k, sel);
+  else if (k <= 16)
+    topk_kernel<15><<<grid, block, 0, stream>>>(P, ldp, nrows, Nq, H_kv, q_start, nblk_dec, k, sel);
+  else
+    topk_kernel<31><<<grid, block, 0, stream>>>(P, ldp, nrows, Nq, H_kv, q_start, nblk_dec, k, sel);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_prefill(const float* P, int64_t ldp, int64_t q_start, int64_t Nq,
+                               int H_kv, int k, int32_t* sel, hipStream_t stream) {
+  return launch_topk(P, ldp, (int64_t)H_kv * Nq, Nq, H_kv, q_start, 0, k, sel, stream);
+}
+
+hipError_t launch_topk_decode(const float* P, int64_t ldp, int B, int H_kv, int nblk, int k,
+                              int32_t* sel, hipStream_t stream) {
+  return launch_topk(P, ldp, (int64_t)B * H_kv, 1, H_kv, 0, nblk, k, sel, stream);
+}
+
+hipError_t launch_index_topk_fused(const void*, const void*, int64_t, int64_t, int, int, int,
+                                   int32_t*, hipStream_t) {
+  return hipErrorNotSupported;
+}
+
+}  // namespace msa

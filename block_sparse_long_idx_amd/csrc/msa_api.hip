@@ -1,0 +1,413 @@
+// C ABI of libmsa: argument validation, workspace layout and the launch
+// sequence of each entry point.  Every check runs on the host before any
+// work is enqueued; nothing here allocates device memory or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/msa.h"
+#include "msa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+int64_t g_opt_fused = 0;
+int64_t g_opt_chunk = 1024;
+
+constexpr int kB = 128;
+constexpr size_t kAlign = 256;
+
+msa_status fail(msa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+msa_status ok() {
+  g_err.clear();
+  return MSA_OK;
+}
+
+msa_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return MSA_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Sub-allocator over a caller-provided workspace.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* p) : base(static_cast<char*>(p)) {}
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+    off = align_up(off + bytes);
+    return p;
+  }
+};
+
+int64_t nnz_of(int64_t q_start, int64_t Nq, int H_kv, int B_k, int k) {
+  // sum over i of min(k, i/B_k + 1): positions with lb < k-1 contribute
+  // lb+1, the rest k.
+  int64_t tot = 0;
+  const int64_t q_end = q_start + Nq;
+  const int64_t full_from = (int64_t)(k - 1) * B_k;  // first i with lb >= k-1
+  for (int64_t b = q_start / B_k; b * B_k < min(q_end, full_from); ++b) {
+    const int64_t lo = max(q_start, b * B_k), hi = min(q_end, min((b + 1) * B_k, full_from));
+    if (hi > lo) tot += (hi - lo) * (b + 1);
+  }
+  if (q_end > full_from) tot += (q_end - max(q_start, full_from)) * k;
+  return tot * H_kv;
+}
+
+msa_status check_common(int64_t q_start, int64_t Nq, int H_kv, int B_k, int k) {
+  if (q_start < 0 || Nq < 1) return fail(MSA_ERR_INVALID_ARG, "need q_start >= 0 and Nq >= 1");
+  if (H_kv < 1) return fail(MSA_ERR_INVALID_ARG, "H_kv must be >= 1");
+  if (H_kv > 64) return fail(MSA_ERR_UNSUPPORTED, "H_kv > 64 is not supported");
+  if (B_k != kB) return fail(MSA_ERR_UNSUPPORTED, "only B_k = 128 is supported (got %d)", B_k);
+  if (k < 1 || k > 32) return fail(MSA_ERR_UNSUPPORTED, "k must be in [1, 32] (got %d)", k);
+  const int64_t nblk = cdiv(q_start + Nq, B_k);
+  if (nblk > 16384) return fail(MSA_ERR_UNSUPPORTED, "more than 16384 key blocks");
+  if (nnz_of(q_start, Nq, H_kv, B_k, k) >= (int64_t)1 << 31)
+    return fail(MSA_ERR_UNSUPPORTED, "selection nnz >= 2^31: use smaller query chunks");
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------- index
+size_t index_ws(int64_t q_start, int64_t Nq, int H_kv) {
+  const int64_t nblk = cdiv(q_start + Nq, kB);
+  const int64_t ldp = cdiv(nblk, 4) * 4;
+  return align_up(sizeof(float) * (size_t)(H_kv * Nq * ldp));
+}
+
+msa_status run_index_topk(const void* q_idx, const void* k_idx, int64_t q_start, int64_t Nq,
+                          int H_kv, int d_idx, int k, int32_t* sel, void* ws,
+                          hipStream_t s) {
+  if (g_opt_fused)
+    return hip_status(
+        msa::launch_index_topk_fused(q_idx, k_idx, q_start, Nq, H_kv, d_idx, k, sel, s),
+        "index/top-k (fused) launch");
+  const int64_t nblk = cdiv(q_start + Nq, kB);
+  const int64_t ldp = cdiv(nblk, 4) * 4;
+  float* P = static_cast<float*>(ws);
+  msa_status st = hip_status(
+      msa::launch_index_pool(q_idx, k_idx, q_start, Nq, H_kv, d_idx, P, ldp, s),
+      "index score launch");
+  if (st) return st;
+  return hip_status(msa::launch_topk_prefill(P, ldp, q_start, Nq, H_kv, k, sel, s),
+                    "top-k launch");
+}
+
+// ---------------------------------------------------------------- invert
+size_t invert_ws(int64_t q_start, int64_t Nq, int H_kv) {
+  const int nblk = (int)cdiv(q_start + Nq, kB);
+  return align_up(msa::invert_scratch_bytes(Nq, H_kv, nblk));
+}
+
+// ---------------------------------------------------------------- attention
+struct AttnWs {
+  int4* items;
+  int32_t* n_items;
+  void* Os;
+  float* lse_s;
+  float* Oloc;
+  int64_t max_items;
+  size_t bytes;
+};
+
+AttnWs attn_layout(void* ws, int64_t q_start, int64_t Nq, int H_q, int H_kv, int d_h, int k) {
+  const int64_t nblk = cdiv(q_start + Nq, kB);
+  const int64_t nnz = nnz_of(q_start, Nq, H_kv, kB, k);
+  AttnWs w;
+  Carve c(ws);
+  w.max_items = msa::attn_max_items((int64_t)H_kv * nblk, nnz, (int)g_opt_chunk);
+  w.items = c.take<int4>(sizeof(int4) * (size_t)w.max_items);
+  w.n_items = c.take<int32_t>(sizeof(int32_t));
+  w.Os = c.take<void>(2 * (size_t)Nq * (k - 1) * H_q * d_h);
+  w.lse_s = c.take<float>(sizeof(float) * (size_t)Nq * k * H_q);
+  w.Oloc = c.take<float>(sizeof(float) * (size_t)Nq * H_q * d_h);
+  w.bytes = c.off;
+  return w;
+}
+
+msa_status check_attn_shapes(int H_q, int H_kv, int d_h) {
+  if (H_q < 1 || H_q % H_kv) return fail(MSA_ERR_INVALID_ARG, "H_q must be a positive multiple of H_kv");
+  if (d_h != 64 && d_h != 128) return fail(MSA_ERR_UNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
+  return MSA_OK;
+}
+
+msa_status run_attn(const void* Q, const void* K, const void* V, const int32_t* row_ptr,
+                    const int32_t* col, const uint8_t* slot, int64_t q_start, int64_t Nq,
+                    int64_t Nk, int H_q, int H_kv, int d_h, int k, float scale, float* O,
+                    float* lse, void* ws, hipStream_t s) {
+  const int nblk = (int)cdiv(q_start + Nq, kB);
+  AttnWs w = attn_layout(ws, q_start, Nq, H_q, H_kv, d_h, k);
+  msa_status st = hip_status(msa::launch_build_items(row_ptr, (int64_t)H_kv * nblk, nblk,
+                                                     q_start, Nq, (int)g_opt_chunk, w.items,
+                                                     w.n_items, s),
+                             "work-list launch");
+  if (st) return st;
+  st = hip_status(msa::launch_attn(Q, K, V, col, slot, w.items, w.n_items, w.max_items, q_start,
+                                   Nk, H_q, H_kv, d_h, nblk, k, scale, w.Os, w.lse_s, w.Oloc, s),
+                  "attention launch");
+  if (st) return st;
+  return hip_status(
+      msa::launch_combine(w.Os, w.lse_s, w.Oloc, q_start, Nq, H_q, d_h, k, O, lse, s),
+      "combine launch");
+}
+
+msa_status check_index_dims(int d_idx) {
+  if (d_idx != 32 && d_idx != 64 && d_idx != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "d_idx must be 32, 64 or 128 (got %d)", d_idx);
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------- prefill
+struct PrefillWs {
+  int32_t* sel;  // chunk buffer when the caller passes no sel
+  int32_t* row_ptr;
+  int32_t* col;
+  uint8_t* slot;
+  void* shared;
+  size_t bytes;
+};
+
+PrefillWs prefill_layout(void* ws, int64_t N, int64_t chunk, int H_q, int H_kv, int d_h, int k,
+                         bool own_sel) {
+  const int64_t nblk = cdiv(N, kB);
+  int64_t nnz_max = 0;
+  size_t shared = 0;
+  for (int64_t q0 = 0; q0 < N; q0 += chunk) {
+    const int64_t nq = std::min(chunk, N - q0);
+    nnz_max = std::max(nnz_max, nnz_of(q0, nq, H_kv, kB, k));
+    shared = std::max(shared, index_ws(q0, nq, H_kv));
+    shared = std::max(shared, invert_ws(q0, nq, H_kv));
+    shared = std::max(shared, attn_layout(nullptr, q0, nq, H_q, H_kv, d_h, k).bytes);
+  }
+  PrefillWs w;
+  Carve c(ws);
+  w.sel = own_sel ? c.take<int32_t>(sizeof(int32_t) * (size_t)chunk * H_kv * k) : nullptr;
+  w.row_ptr = c.take<int32_t>(sizeof(int32_t) * (size_t)(H_kv * nblk + 1));
+  w.col = c.take<int32_t>(sizeof(int32_t) * (size_t)nnz_max);
+  w.slot = c.take<uint8_t>((size_t)nnz_max);
+  w.shared = c.take<void>(shared);
+  w.bytes = c.off;
+  return w;
+}
+
+// ---------------------------------------------------------------- decode
+struct DecodeWs {
+  float* P;
+  int64_t ldp;
+  float* Opart;
+  float* lse_part;
+  size_t bytes;
+};
+
+DecodeWs decode_layout(void* ws, int B, int64_t N, int H_q, int H_kv, int d_h, int k) {
+  const int64_t nblk = cdiv(N, kB);
+  DecodeWs w;
+  Carve c(ws);
+  w.ldp = cdiv(nblk, 4) * 4;
+  w.P = c.take<float>(sizeof(float) * (size_t)B * H_kv * w.ldp);
+  w.Opart = c.take<float>(sizeof(float) * (size_t)B * H_q * k * d_h);
+  w.lse_part = c.take<float>(sizeof(float) * (size_t)B * H_q * k);
+  w.bytes = c.off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_last_error(void) { return g_err.c_str(); }
+
+int64_t msa_selection_nnz(int64_t q_start, int64_t Nq, int H_kv, int B_k, int k) {
+  if (q_start < 0 || Nq < 0 || H_kv < 1 || B_k < 1 || k < 1) return -1;
+  return nnz_of(q_start, Nq, H_kv, B_k, k);
+}
+
+size_t msa_index_topk_workspace_bytes(int64_t q_start, int64_t Nq, int H_kv, int B_k, int k) {
+  if (check_common(q_start, Nq, H_kv, B_k, k)) return 0;
+  return index_ws(q_start, Nq, H_kv);
+}
+
+msa_status msa_index_topk(const void* q_idx, const void* k_idx, int64_t q_start, int64_t Nq,
+                          int64_t Nk, int H_kv, int d_idx, int B_k, int k, int32_t* sel,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (msa_status st = check_common(q_start, Nq, H_kv, B_k, k)) return st;
+  if (msa_status st = check_index_dims(d_idx)) return st;
+  if (!q_idx || !k_idx || !sel) return fail(MSA_ERR_INVALID_ARG, "null q_idx, k_idx or sel");
+  if (Nk < q_start + Nq) return fail(MSA_ERR_INVALID_ARG, "Nk must be >= q_start + Nq");
+  if (!g_opt_fused && (!ws || ws_bytes < index_ws(q_start, Nq, H_kv)))
+    return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", index_ws(q_start, Nq, H_kv));
+  msa_status st = run_index_topk(q_idx, k_idx, q_start, Nq, H_kv, d_idx, k, sel, ws,
+                                 static_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+size_t msa_invert_index_workspace_bytes(int64_t q_start, int64_t Nq, int H_kv, int B_k, int k) {
+  if (check_common(q_start, Nq, H_kv, B_k, k)) return 0;
+  return invert_ws(q_start, Nq, H_kv);
+}
+
+msa_status msa_invert_index(const int32_t* sel, int64_t q_start, int64_t Nq, int H_kv, int B_k,
+                            int k, int32_t* row_ptr, int32_t* col, uint8_t* slot, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (msa_status st = check_common(q_start, Nq, H_kv, B_k, k)) return st;
+  if (!sel || !row_ptr || !col || !slot)
+    return fail(MSA_ERR_INVALID_ARG, "null sel, row_ptr, col or slot");
+  if (!ws || ws_bytes < invert_ws(q_start, Nq, H_kv))
+    return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", invert_ws(q_start, Nq, H_kv));
+  const int nblk = (int)cdiv(q_start + Nq, B_k);
+  msa_status st = hip_status(msa::launch_invert(sel, q_start, Nq, H_kv, k, nblk, row_ptr, col,
+                                                slot, ws, static_cast<hipStream_t>(stream)),
+                             "inverted-index launch");
+  return st ? st : ok();
+}
+
+size_t msa_sparse_attn_fwd_workspace_bytes(int64_t q_start, int64_t Nq, int H_q, int H_kv,
+                                           int d_h, int B_k, int k) {
+  if (check_common(q_start, Nq, H_kv, B_k, k) || check_attn_shapes(H_q, H_kv, d_h)) return 0;
+  return attn_layout(nullptr, q_start, Nq, H_q, H_kv, d_h, k).bytes;
+}
+
+msa_status msa_sparse_attn_fwd(const void* Q, const void* K, const void* V,
+                               const int32_t* row_ptr, const int32_t* col, const uint8_t* slot,
+                               int64_t q_start, int64_t Nq, int64_t Nk, int H_q, int H_kv,
+                               int d_h, int B_k, int k, float scale, float* O, float* lse,
+                               void* ws, size_t ws_bytes, void* stream) {
+  if (msa_status st = check_common(q_start, Nq, H_kv, B_k, k)) return st;
+  if (msa_status st = check_attn_shapes(H_q, H_kv, d_h)) return st;
+  if (!Q || !K || !V || !row_ptr || !col || !slot || !O)
+    return fail(MSA_ERR_INVALID_ARG, "null Q, K, V, row_ptr, col, slot or O");
+  if (Nk < q_start + Nq) return fail(MSA_ERR_INVALID_ARG, "Nk must be >= q_start + Nq");
+  if (!(scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "scale must be > 0");
+  const size_t need = attn_layout(nullptr, q_start, Nq, H_q, H_kv, d_h, k).bytes;
+  if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  msa_status st = run_attn(Q, K, V, row_ptr, col, slot, q_start, Nq, Nk, H_q, H_kv, d_h, k,
+                           scale, O, lse, ws, static_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+size_t msa_prefill_workspace_bytes(int64_t N, int64_t chunk, int H_q, int H_kv, int d_h,
+                                   int d_idx, int B_k, int k) {
+  (void)d_idx;
+  if (N < 1) return 0;
+  if (chunk <= 0 || chunk > N) chunk = N;
+  if (check_common(0, N, H_kv, B_k, k) || check_attn_shapes(H_q, H_kv, d_h)) return 0;
+  return prefill_layout(nullptr, N, chunk, H_q, H_kv, d_h, k, true).bytes;
+}
+
+msa_status msa_prefill(const void* Q, const void* K, const void* V, const void* q_idx,
+                       const void* k_idx, int64_t N, int64_t chunk, int H_q, int H_kv, int d_h,
+                       int d_idx, int B_k, int k, float scale, int32_t* sel, float* O,
+                       float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (N < 1) return fail(MSA_ERR_INVALID_ARG, "N must be >= 1");
+  if (chunk < 0) return fail(MSA_ERR_INVALID_ARG, "chunk must be >= 0");
+  if (chunk == 0 || chunk > N) chunk = N;
+  if (msa_status st = check_common(0, N, H_kv, B_k, k)) return st;
+  if (msa_status st = check_attn_shapes(H_q, H_kv, d_h)) return st;
+  if (msa_status st = check_index_dims(d_idx)) return st;
+  if (!Q || !K || !V || !q_idx || !k_idx || !O)
+    return fail(MSA_ERR_INVALID_ARG, "null Q, K, V, q_idx, k_idx or O");
+  if (!(scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "scale must be > 0");
+  const bool own_sel = sel == nullptr;
+  const size_t need = prefill_layout(nullptr, N, chunk, H_q, H_kv, d_h, k, true).bytes;
+  if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  PrefillWs w = prefill_layout(ws, N, chunk, H_q, H_kv, d_h, k, own_sel);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t q0 = 0; q0 < N; q0 += chunk) {
+    const int64_t nq = std::min(chunk, N - q0);
+    int32_t* sel_c = own_sel ? w.sel : sel + q0 * H_kv * k;
+    msa_status st = run_index_topk(q_idx, k_idx, q0, nq, H_kv, d_idx, k, sel_c, w.shared, s);
+    if (st) return st;
+    const int nblk = (int)cdiv(q0 + nq, kB);
+    st = hip_status(msa::launch_invert(sel_c, q0, nq, H_kv, k, nblk, w.row_ptr, w.col, w.slot,
+                                       w.shared, s),
+                    "inverted-index launch");
+    if (st) return st;
+    st = run_attn(Q, K, V, w.row_ptr, w.col, w.slot, q0, nq, N, H_q, H_kv, d_h, k, scale,
+                  O + q0 * H_q * d_h, lse ? lse + q0 * H_q : nullptr, w.shared, s);
+    if (st) return st;
+  }
+  return ok();
+}
+
+size_t msa_decode_workspace_bytes(int B, int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
+  if (B < 1 || N < 1 || check_common(0, N, H_kv, B_k, k) || check_attn_shapes(H_q, H_kv, d_h))
+    return 0;
+  return decode_layout(nullptr, B, N, H_q, H_kv, d_h, k).bytes;
+}
+
+msa_status msa_decode(const void* q, const void* q_idx, const void* K, const void* V,
+                      const void* k_idx, int B, int64_t N, int H_q, int H_kv, int d_h, int d_idx,
+                      int B_k, int k, float scale, int32_t* sel, float* O, float* lse, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (B < 1 || N < 1) return fail(MSA_ERR_INVALID_ARG, "need B >= 1 and N >= 1");
+  if (msa_status st = check_common(0, N, H_kv, B_k, k)) return st;
+  if (msa_status st = check_attn_shapes(H_q, H_kv, d_h)) return st;
+  if (msa_status st = check_index_dims(d_idx)) return st;
+  if (64 % H_kv) return fail(MSA_ERR_UNSUPPORTED, "decode needs H_kv to divide 64");
+  if (!q || !q_idx || !K || !V || !k_idx || !sel || !O)
+    return fail(MSA_ERR_INVALID_ARG, "null q, q_idx, K, V, k_idx, sel or O");
+  if (!(scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "scale must be > 0");
+  const size_t need = decode_layout(nullptr, B, N, H_q, H_kv, d_h, k).bytes;
+  if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  DecodeWs w = decode_layout(ws, B, N, H_q, H_kv, d_h, k);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nblk = (int)cdiv(N, kB);
+  msa_status st = MSA_OK;
+  if (nblk > 1)
+    st = hip_status(msa::launch_decode_scan(q_idx, k_idx, B, N, H_kv, d_idx, nblk, w.P, w.ldp, s),
+                    "decode scan launch");
+  if (st) return st;
+  st = hip_status(msa::launch_topk_decode(w.P, w.ldp, B, H_kv, nblk, k, sel, s),
+                  "decode top-k launch");
+  if (st) return st;
+  st = hip_status(msa::launch_decode_attn(q, K, V, sel, B, N, H_q, H_kv, d_h, k, scale, w.Opart,
+                                          w.lse_part, s),
+                  "decode attention launch");
+  if (st) return st;
+  st = hip_status(msa::launch_decode_merge(w.Opart, w.lse_part, B, H_q, d_h, k,
+                                           std::min(k, nblk), O, lse, s),
+                  "decode merge launch");
+  return st ? st : ok();
+}
+
+msa_status msa_set_option(int option, int64_t value) {
+  switch (option) {
+    case MSA_OPT_INDEX_FUSED:
+      if (value != 0 && value != 1) return fail(MSA_ERR_INVALID_ARG, "fused must be 0 or 1");
+      g_opt_fused = value;
+      return ok();
+    case MSA_OPT_ATTN_CHUNK:
+      if (value < 1 || value > (1 << 20)) return fail(MSA_ERR_INVALID_ARG, "chunk out of range");
+      g_opt_chunk = value;
+      return ok();
+    default:
+      return fail(MSA_ERR_INVALID_ARG, "unknown option %d", option);
+  }
+}
+
+int64_t msa_get_option(int option) {
+  switch (option) {
+    case MSA_OPT_INDEX_FUSED:
+      return g_opt_fused;
+    case MSA_OPT_ATTN_CHUNK:
+      return g_opt_chunk;
+    default:
+      return -1;
+  }
+}
+
+}  // extern "C"

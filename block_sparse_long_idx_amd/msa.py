@@ -1,0 +1,230 @@
+"""ctypes binding of libmsa (include/msa.h): argument marshalling only.
+
+Every step of the MSA forward path runs in libmsa's HIP kernels; torch
+supplies device memory (outputs and workspaces) and the current stream.
+There is no CPU fallback: if libmsa.so is missing or no GPU is present the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmsa.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "msa.h")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OPT_INDEX_FUSED, OPT_ATTN_CHUNK = 1, 2
+B_K = 128
+
+_lib = None
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libmsa status {status}: {message}")
+        self.status = status
+
+
+def load():
+    """Load libmsa.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i64, i32, sz, f32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                            ctypes.c_size_t, ctypes.c_float)
+    sigs = {
+        "msa_last_error": ([], ctypes.c_char_p),
+        "msa_selection_nnz": ([i64, i64, i32, i32, i32], i64),
+        "msa_index_topk_workspace_bytes": ([i64, i64, i32, i32, i32], sz),
+        "msa_index_topk": ([P, P, i64, i64, i64, i32, i32, i32, i32, P, P, sz, P], i32),
+        "msa_invert_index_workspace_bytes": ([i64, i64, i32, i32, i32], sz),
+        "msa_invert_index": ([P, i64, i64, i32, i32, i32, P, P, P, P, sz, P], i32),
+        "msa_sparse_attn_fwd_workspace_bytes": ([i64, i64, i32, i32, i32, i32, i32], sz),
+        "msa_sparse_attn_fwd": ([P, P, P, P, P, P, i64, i64, i64, i32, i32, i32, i32,
+                                 i32, f32, P, P, P, sz, P], i32),
+        "msa_prefill_workspace_bytes": ([i64, i64, i32, i32, i32, i32, i32, i32], sz),
+        "msa_prefill": ([P, P, P, P, P, i64, i64, i32, i32, i32, i32, i32, i32, f32, P,
+                         P, P, P, sz, P], i32),
+        "msa_decode_workspace_bytes": ([i32, i64, i32, i32, i32, i32, i32], sz),
+        "msa_decode": ([P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32, f32, P, P,
+                        P, P, sz, P], i32),
+        "msa_set_option": ([i32, i64], i32),
+        "msa_get_option": ([i32], i64),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def header_functions():
+    """Names of the functions declared in include/msa.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != OK:
+        raise MsaError(status, load().msa_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("libmsa works on GPU tensors only")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def set_option(option: int, value: int):
+    _check(load().msa_set_option(option, value))
+
+
+def get_option(option: int) -> int:
+    return load().msa_get_option(option)
+
+
+def selection_nnz(q_start, Nq, H_kv, k, B_k=B_K) -> int:
+    return load().msa_selection_nnz(q_start, Nq, H_kv, B_k, k)
+
+
+def index_topk(q_idx, k_idx, k, q_start=0, Nq=None, B_k=B_K, sel=None, ws=None):
+    """Index Branch for query rows [q_start, q_start+Nq): returns sel int32
+    [Nq, H_kv, k].  q_idx/k_idx: bf16 [N, H_kv, d_idx] on the GPU."""
+    _need_cuda(q_idx, k_idx)
+    N, H_kv, d_idx = k_idx.shape
+    Nq = q_idx.shape[0] - q_start if Nq is None else Nq
+    lib = load()
+    if sel is None:
+        sel = torch.empty((Nq, H_kv, k), dtype=torch.int32, device=k_idx.device)
+    need = lib.msa_index_topk_workspace_bytes(q_start, Nq, H_kv, B_k, k)
+    if ws is None:
+        ws = _workspace(need, k_idx.device)
+    _check(lib.msa_index_topk(_ptr(q_idx), _ptr(k_idx), q_start, Nq, N, H_kv, d_idx, B_k,
+                              k, _ptr(sel), _ptr(ws), ws.numel(), _stream(k_idx)))
+    return sel
+
+
+def invert_index(sel, q_start=0, B_k=B_K, ws=None):
+    """Inverted index of sel [Nq, H_kv, k]: (row_ptr, col int32, slot uint8)."""
+    _need_cuda(sel)
+    Nq, H_kv, k = sel.shape
+    lib = load()
+    nblk = (q_start + Nq + B_k - 1) // B_k
+    nnz = lib.msa_selection_nnz(q_start, Nq, H_kv, B_k, k)
+    dev = sel.device
+    row_ptr = torch.empty(H_kv * nblk + 1, dtype=torch.int32, device=dev)
+    col = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+    slot = torch.empty(max(nnz, 1), dtype=torch.uint8, device=dev)
+    need = lib.msa_invert_index_workspace_bytes(q_start, Nq, H_kv, B_k, k)
+    if ws is None:
+        ws = _workspace(need, dev)
+    _check(lib.msa_invert_index(_ptr(sel), q_start, Nq, H_kv, B_k, k, _ptr(row_ptr),
+                                _ptr(col), _ptr(slot), _ptr(ws), ws.numel(), _stream(sel)))
+    return row_ptr, col[:nnz], slot[:nnz]
+
+
+def sparse_attn_fwd(Q, K, V, row_ptr, col, slot, k, q_start=0, Nq=None, scale=None,
+                    B_k=B_K, want_lse=True, O=None, lse=None, ws=None):
+    """Main Branch for query rows [q_start, q_start+Nq): (O fp32, lse fp32)."""
+    _need_cuda(Q, K, V, row_ptr, col, slot)
+    Nk, H_kv, d_h = K.shape
+    H_q = Q.shape[1]
+    Nq = Q.shape[0] - q_start if Nq is None else Nq
+    scale = 1.0 / math.sqrt(d_h) if scale is None else scale
+    lib = load()
+    dev = Q.device
+    if O is None:
+        O = torch.empty((Nq, H_q, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((Nq, H_q), dtype=torch.float32, device=dev)
+    need = lib.msa_sparse_attn_fwd_workspace_bytes(q_start, Nq, H_q, H_kv, d_h, B_k, k)
+    if ws is None:
+        ws = _workspace(need, dev)
+    _check(lib.msa_sparse_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(row_ptr), _ptr(col),
+                                   _ptr(slot), q_start, Nq, Nk, H_q, H_kv, d_h, B_k, k,
+                                   scale, _ptr(O), _ptr(lse), _ptr(ws), ws.numel(),
+                                   _stream(Q)))
+    return O, lse
+
+
+def prefill_workspace_bytes(N, H_q, H_kv, d_h, d_idx, k, chunk=0, B_k=B_K) -> int:
+    return load().msa_prefill_workspace_bytes(N, chunk, H_q, H_kv, d_h, d_idx, B_k, k)
+
+
+def prefill(Q, K, V, q_idx, k_idx, k, scale=None, chunk=0, B_k=B_K, want_sel=True,
+            want_lse=True, sel=None, O=None, lse=None, ws=None):
+    """Whole prefill over query chunks: (sel, O, lse)."""
+    _need_cuda(Q, K, V, q_idx, k_idx)
+    N, H_q, d_h = Q.shape
+    H_kv, d_idx = k_idx.shape[1], k_idx.shape[2]
+    scale = 1.0 / math.sqrt(d_h) if scale is None else scale
+    lib = load()
+    dev = Q.device
+    if sel is None and want_sel:
+        sel = torch.empty((N, H_kv, k), dtype=torch.int32, device=dev)
+    if O is None:
+        O = torch.empty((N, H_q, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((N, H_q), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(lib.msa_prefill_workspace_bytes(N, chunk, H_q, H_kv, d_h, d_idx,
+                                                        B_k, k), dev)
+    _check(lib.msa_prefill(_ptr(Q), _ptr(K), _ptr(V), _ptr(q_idx), _ptr(k_idx), N, chunk,
+                           H_q, H_kv, d_h, d_idx, B_k, k, scale, _ptr(sel), _ptr(O),
+                           _ptr(lse), _ptr(ws), ws.numel(), _stream(Q)))
+    return sel, O, lse
+
+
+def decode_workspace_bytes(B, N, H_q, H_kv, d_h, k, B_k=B_K) -> int:
+    return load().msa_decode_workspace_bytes(B, N, H_q, H_kv, d_h, B_k, k)
+
+
+def decode(q, q_idx, K, V, k_idx, k, scale=None, B_k=B_K, want_lse=True, sel=None,
+           O=None, lse=None, ws=None):
+    """Decode step for B sequences (query = last cache row): (sel, O, lse)."""
+    _need_cuda(q, q_idx, K, V, k_idx)
+    B, N, H_kv, d_h = K.shape
+    H_q = q.shape[1]
+    d_idx = k_idx.shape[3]
+    scale = 1.0 / math.sqrt(d_h) if scale is None else scale
+    lib = load()
+    dev = q.device
+    if sel is None:
+        sel = torch.empty((B, H_kv, k), dtype=torch.int32, device=dev)
+    if O is None:
+        O = torch.empty((B, H_q, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H_q), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(lib.msa_decode_workspace_bytes(B, N, H_q, H_kv, d_h, B_k, k), dev)
+    _check(lib.msa_decode(_ptr(q), _ptr(q_idx), _ptr(K), _ptr(V), _ptr(k_idx), B, N, H_q,
+                          H_kv, d_h, d_idx, B_k, k, scale, _ptr(sel), _ptr(O), _ptr(lse),
+                          _ptr(ws), ws.numel(), _stream(q)))
+    return sel, O, lse

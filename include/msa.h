@@ -1,0 +1,186 @@
+/*
+ * msa.h -- C ABI of libmsa, the MiniMax Sparse Attention (MSA) forward path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "MiniMax Sparse Attention" explainer
+ * (minimax-sparse-attention-danialwang.pages.dev) and the paper abstract
+ * (arXiv 2606.13392).  Attention is split into an Index Branch, which
+ * picks for every query position i and GQA group r a set of k key blocks
+ * of B_k tokens (always including the query's own "local" block), and a
+ * Main Branch, which runs exact softmax attention over the tokens of
+ * those blocks only (section 02; Figure 1 caption).
+ *
+ * Notation (section 01, section 04): N tokens, H_q query heads, H_kv KV
+ * heads (= GQA groups), G = H_q / H_kv adjacent query heads per group
+ * (head h is in group floor(h / G)), head dim d_h, index dim d_idx, block
+ * size B_k, k blocks per (query, group).  Positions are 0-based; query i
+ * sees keys j <= i; its local block is floor(i / B_k).
+ *
+ * Layouts: every tensor is dense, row-major, token-major:
+ *   Q [N, H_q, d_h] bf16           K, V [N, H_kv, d_h] bf16
+ *   q_idx, k_idx [N, H_kv, d_idx] bf16 (one index head per group)
+ *   sel [Nq, H_kv, k] int32: ascending block ids, -1 padded
+ *   O [Nq, H_q, d_h] fp32          lse [Nq, H_q] fp32 (natural log)
+ * All pointers are device pointers unless stated otherwise.
+ *
+ * Ownership: the caller owns every buffer, including the workspaces sized
+ * by the *_workspace_bytes functions.  The library allocates and frees
+ * nothing, never synchronises, and keeps no per-call device state; all
+ * work is enqueued on `stream` (a hipStream_t; NULL = default stream).
+ *
+ * Errors: arguments are checked on the host before anything is enqueued.
+ * A bad argument returns MSA_ERR_INVALID_ARG, an unsupported shape
+ * MSA_ERR_UNSUPPORTED, a short workspace MSA_ERR_WORKSPACE, all without
+ * touching the device; a failed launch returns MSA_ERR_HIP.  The reason is
+ * kept per thread and read with msa_last_error().
+ *
+ * Supported shapes: B_k = 128; d_h in {64, 128}; d_idx in {32, 64, 128};
+ * 1 <= k <= 32; H_q a multiple of H_kv; H_kv <= 64; every block count
+ * ceil(N / B_k) <= 16384; every selection nnz < 2^31.
+ *
+ * Determinism: every output is bitwise identical from run to run.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int msa_status;
+#define MSA_OK 0
+#define MSA_ERR_INVALID_ARG (-1)
+#define MSA_ERR_UNSUPPORTED (-2)
+#define MSA_ERR_WORKSPACE (-3)
+#define MSA_ERR_HIP (-4)
+
+/* Message for the last non-OK status returned on this thread ("" if none).
+ * The string stays valid until the next libmsa call on the thread. */
+const char *msa_last_error(void);
+
+/* Number of (query, group, selected block) entries of a selection table
+ * for query positions q_start .. q_start+Nq-1: H_kv * sum_i min(k, i/B_k+1).
+ * (Section 04: every query reads a fixed budget of k blocks, fewer only
+ * while fewer are visible.)  Returns -1 on bad arguments. */
+int64_t msa_selection_nnz(int64_t q_start, int64_t Nq, int H_kv, int B_k, int k);
+
+/*
+ * Index Branch (section 02; Figure 1 caption; section 05 part 1).
+ * For each query position i in [q_start, q_start+Nq) and group r:
+ *   token score   S[j] = q_idx[i,r,:] . k_idx[j,r,:]   for j <= i
+ *   block score   P[b] = max of S over block b          (block max pooling)
+ *   selection     sel[i-q_start, r, :] = {lb(i)} plus the k-1 earlier
+ *                 blocks with the largest P, ties to the lower block id;
+ *                 all visible blocks if there are at most k.
+ * Selection uses the raw scores (softmax keeps their order).
+ *   q_idx, k_idx: bases of full-sequence tensors [>= q_start+Nq, H_kv, d_idx]
+ *   Nk:           rows available in k_idx (must be >= q_start+Nq)
+ *   sel:          out, [Nq, H_kv, k] int32
+ *   ws:           device workspace of >= msa_index_topk_workspace_bytes()
+ */
+size_t msa_index_topk_workspace_bytes(int64_t q_start, int64_t Nq, int H_kv,
+                                      int B_k, int k);
+msa_status msa_index_topk(const void *q_idx, const void *k_idx, int64_t q_start,
+                          int64_t Nq, int64_t Nk, int H_kv, int d_idx, int B_k,
+                          int k, int32_t *sel, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/*
+ * Inverted index (section 05 part 2: KV-outer execution gathers, for each
+ * KV block, the queries that selected it).  CSR over buckets (r, b) in
+ * r-major order, nblk = ceil((q_start+Nq)/B_k):
+ *   row_ptr [H_kv*nblk + 1] int32: bucket start offsets, row_ptr[0] = 0
+ *   col     [nnz] int32: absolute query positions, ascending in a bucket
+ *   slot    [nnz] uint8: rank of b inside sel[i-q_start, r, :]
+ * nnz = msa_selection_nnz(q_start, Nq, H_kv, B_k, k).  sel must be a
+ * well-formed selection (as msa_index_topk writes it).
+ */
+size_t msa_invert_index_workspace_bytes(int64_t q_start, int64_t Nq, int H_kv,
+                                        int B_k, int k);
+msa_status msa_invert_index(const int32_t *sel, int64_t q_start, int64_t Nq,
+                            int H_kv, int B_k, int k, int32_t *row_ptr,
+                            int32_t *col, uint8_t *slot, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * Main Branch, KV-outer (section 02; section 05 part 2).  For each query
+ * position i in the chunk and head h (group r = h / G):
+ *   O[i-q_start, h, :] = softmax over the tokens j <= i of the selected
+ *   blocks of scale * Q[i,h,:].K[j,r,:], applied to V[j,r,:]
+ *   lse[i-q_start, h]  = ln sum_j exp(scale * Q[i,h,:].K[j,r,:])
+ * Each selected KV block is read once per work item and the queries that
+ * hit it are gathered through the inverted index; per-block partial
+ * results go to pre-assigned slots and a combine step merges them through
+ * their log-sum-exp in ascending block order (section 05 part 2,
+ * two-phase forward).
+ *   Q, K, V:  bases of full-sequence tensors; Nk rows of K/V available
+ *   row_ptr, col, slot: from msa_invert_index for the same chunk
+ *   O:        out [Nq, H_q, d_h] fp32; lse: out [Nq, H_q] fp32, nullable
+ */
+size_t msa_sparse_attn_fwd_workspace_bytes(int64_t q_start, int64_t Nq, int H_q,
+                                           int H_kv, int d_h, int B_k, int k);
+msa_status msa_sparse_attn_fwd(const void *Q, const void *K, const void *V,
+                               const int32_t *row_ptr, const int32_t *col,
+                               const uint8_t *slot, int64_t q_start, int64_t Nq,
+                               int64_t Nk, int H_q, int H_kv, int d_h, int B_k,
+                               int k, float scale, float *O, float *lse,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Whole prefill: Index Branch, inverted index and Main Branch over query
+ * chunks of `chunk` positions, each against its full causal prefix.  Each
+ * query row depends only on its own prefix, so the result does not depend
+ * on `chunk` (0 = one chunk).  Outputs cover the whole sequence:
+ *   sel [N, H_kv, k] int32 (nullable), O [N, H_q, d_h] fp32,
+ *   lse [N, H_q] fp32 (nullable).
+ */
+size_t msa_prefill_workspace_bytes(int64_t N, int64_t chunk, int H_q, int H_kv,
+                                   int d_h, int d_idx, int B_k, int k);
+msa_status msa_prefill(const void *Q, const void *K, const void *V,
+                       const void *q_idx, const void *k_idx, int64_t N,
+                       int64_t chunk, int H_q, int H_kv, int d_h, int d_idx,
+                       int B_k, int k, float scale, int32_t *sel, float *O,
+                       float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Decode: one new query per sequence at the last cache row (position N-1,
+ * so it sees the whole cache and its local block is the last one).  Same
+ * selection and attention as that prefill row, computed Q-outer: the
+ * index scan of k_idx is split over the cache, then every (sequence,
+ * group, selected block) is one attention piece whose partial results are
+ * merged through their log-sum-exp in ascending block order.
+ *   q [B, H_q, d_h], q_idx [B, H_kv, d_idx] bf16
+ *   K, V [B, N, H_kv, d_h], k_idx [B, N, H_kv, d_idx] bf16
+ *   sel out [B, H_kv, k] int32; O out [B, H_q, d_h] fp32;
+ *   lse out [B, H_q] fp32, nullable
+ */
+size_t msa_decode_workspace_bytes(int B, int64_t N, int H_q, int H_kv, int d_h,
+                                  int B_k, int k);
+msa_status msa_decode(const void *q, const void *q_idx, const void *K,
+                      const void *V, const void *k_idx, int B, int64_t N,
+                      int H_q, int H_kv, int d_h, int d_idx, int B_k, int k,
+                      float scale, int32_t *sel, float *O, float *lse, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/*
+ * Tuning knobs (process-wide; they change speed, never results).
+ *   MSA_OPT_INDEX_FUSED: 1 = Index Branch as one kernel that keeps a
+ *     running Top-k per query next to the score GEMM; 0 = GEMM writes the
+ *     block scores, a separate wavefront-per-row Top-k reads them.
+ *   MSA_OPT_ATTN_CHUNK: max query positions per KV-outer work item
+ *     (section 05 part 2: hot blocks are cut along the query dimension).
+ * Returns MSA_ERR_INVALID_ARG for an unknown option or value.
+ */
+#define MSA_OPT_INDEX_FUSED 1
+#define MSA_OPT_ATTN_CHUNK 2
+msa_status msa_set_option(int option, int64_t value);
+int64_t msa_get_option(int option);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -1,0 +1,115 @@
+"""CPU checks of the C ABI: the library loads, exports what include/msa.h
+declares, sizes workspaces, and rejects bad arguments on the host before
+any device work (none of these calls reaches the GPU)."""
+import ctypes
+
+import pytest
+
+from block_sparse_long_idx_amd import msa
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+NULL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return msa.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = msa.header_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_selection_nnz_closed_form(lib):
+    for q_start, Nq, H_kv, k in [(0, 1024, 1, 4), (0, 8192, 4, 16), (300, 5000, 3, 7),
+                                 (65536 * 3, 65536, 4, 16), (0, 1, 2, 1)]:
+        brute = H_kv * sum(min(k, i // 128 + 1) for i in range(q_start, q_start + Nq))
+        assert msa.selection_nnz(q_start, Nq, H_kv, k) == brute
+    # the budget formula for aligned full-size sequences
+    nb = 8192 // 128
+    assert msa.selection_nnz(0, 8192, 1, 16) == 128 * (16 * 15 // 2 + 16 * (nb - 16 + 1))
+
+
+def test_workspace_sizes(lib):
+    assert lib.msa_index_topk_workspace_bytes(0, 8192, 4, 128, 16) >= 4 * 8192 * 64 * 4
+    assert lib.msa_index_topk_workspace_bytes(0, 8192, 4, 64, 16) == 0   # unsupported B_k
+    assert lib.msa_invert_index_workspace_bytes(0, 8192, 4, 128, 16) > 0
+    assert lib.msa_sparse_attn_fwd_workspace_bytes(0, 8192, 64, 4, 128, 128, 16) > \
+        2 * 8192 * 15 * 64 * 128
+    assert lib.msa_sparse_attn_fwd_workspace_bytes(0, 8192, 64, 4, 96, 128, 16) == 0
+    assert lib.msa_prefill_workspace_bytes(1 << 20, 65536, 64, 4, 128, 64, 128, 16) > 0
+    assert lib.msa_decode_workspace_bytes(32, 1 << 20, 64, 4, 128, 128, 16) > 0
+
+
+def _err(lib):
+    return lib.msa_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status", [
+    # q_idx, k_idx, q_start, Nq, Nk, H_kv, d_idx, B_k, k, sel, ws, ws_bytes
+    ((FAKE, FAKE, 0, 0, 128, 1, 64, 128, 4, FAKE, FAKE, 1 << 30), msa.ERR_INVALID_ARG),
+    ((FAKE, FAKE, 0, 128, 128, 1, 64, 64, 4, FAKE, FAKE, 1 << 30), msa.ERR_UNSUPPORTED),
+    ((FAKE, FAKE, 0, 128, 128, 1, 64, 128, 33, FAKE, FAKE, 1 << 30), msa.ERR_UNSUPPORTED),
+    ((FAKE, FAKE, 0, 128, 128, 1, 64, 128, 0, FAKE, FAKE, 1 << 30), msa.ERR_UNSUPPORTED),
+    ((FAKE, FAKE, 0, 128, 128, 1, 48, 128, 4, FAKE, FAKE, 1 << 30), msa.ERR_UNSUPPORTED),
+    ((NULL, FAKE, 0, 128, 128, 1, 64, 128, 4, FAKE, FAKE, 1 << 30), msa.ERR_INVALID_ARG),
+    ((FAKE, FAKE, 0, 128, 100, 1, 64, 128, 4, FAKE, FAKE, 1 << 30), msa.ERR_INVALID_ARG),
+    ((FAKE, FAKE, 0, 128, 128, 1, 64, 128, 4, FAKE, FAKE, 16), msa.ERR_WORKSPACE),
+    ((FAKE, FAKE, 0, 1 << 22, 1 << 22, 1, 64, 128, 4, FAKE, FAKE, 1 << 40),
+     msa.ERR_UNSUPPORTED),   # more than 16384 blocks
+])
+def test_index_topk_rejects(lib, args, status):
+    assert lib.msa_index_topk(*args, NULL) == status
+    assert _err(lib)
+
+
+def test_invert_rejects(lib):
+    assert lib.msa_invert_index(NULL, 0, 128, 1, 128, 4, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                NULL) == msa.ERR_INVALID_ARG
+    assert lib.msa_invert_index(FAKE, 0, 128, 1, 128, 4, FAKE, FAKE, FAKE, FAKE, 4,
+                                NULL) == msa.ERR_WORKSPACE
+
+
+def test_attn_rejects(lib):
+    base = [FAKE] * 6
+    # H_q not a multiple of H_kv
+    assert lib.msa_sparse_attn_fwd(*base, 0, 128, 128, 6, 4, 128, 128, 4, 0.1, FAKE, NULL,
+                                   FAKE, 1 << 30, NULL) == msa.ERR_INVALID_ARG
+    # d_h unsupported
+    assert lib.msa_sparse_attn_fwd(*base, 0, 128, 128, 8, 4, 96, 128, 4, 0.1, FAKE, NULL,
+                                   FAKE, 1 << 30, NULL) == msa.ERR_UNSUPPORTED
+    # bad scale
+    assert lib.msa_sparse_attn_fwd(*base, 0, 128, 128, 8, 4, 128, 128, 4, -1.0, FAKE, NULL,
+                                   FAKE, 1 << 30, NULL) == msa.ERR_INVALID_ARG
+    # workspace too small
+    assert lib.msa_sparse_attn_fwd(*base, 0, 128, 128, 8, 4, 128, 128, 4, 0.1, FAKE, NULL,
+                                   FAKE, 8, NULL) == msa.ERR_WORKSPACE
+
+
+def test_prefill_and_decode_reject(lib):
+    five = [FAKE] * 5
+    assert lib.msa_prefill(*five, 0, 0, 8, 4, 128, 64, 128, 4, 0.1, NULL, FAKE, NULL, FAKE,
+                           1 << 30, NULL) == msa.ERR_INVALID_ARG
+    assert lib.msa_prefill(*five, 1024, -1, 8, 4, 128, 64, 128, 4, 0.1, NULL, FAKE, NULL,
+                           FAKE, 1 << 30, NULL) == msa.ERR_INVALID_ARG
+    assert lib.msa_prefill(*five, 1024, 0, 8, 4, 128, 64, 128, 4, 0.1, NULL, FAKE, NULL,
+                           FAKE, 64, NULL) == msa.ERR_WORKSPACE
+    assert lib.msa_decode(*five, 2, 1024, 12, 3, 128, 64, 128, 4, 0.1, FAKE, FAKE, NULL,
+                          FAKE, 1 << 30, NULL) == msa.ERR_UNSUPPORTED   # 3 does not divide 64
+    assert lib.msa_decode(*five, 0, 1024, 8, 4, 128, 64, 128, 4, 0.1, FAKE, FAKE, NULL,
+                          FAKE, 1 << 30, NULL) == msa.ERR_INVALID_ARG
+
+
+def test_options(lib):
+    assert msa.get_option(msa.OPT_ATTN_CHUNK) >= 1
+    with pytest.raises(msa.MsaError):
+        msa.set_option(99, 1)
+    with pytest.raises(msa.MsaError):
+        msa.set_option(msa.OPT_ATTN_CHUNK, 0)
+    old = msa.get_option(msa.OPT_ATTN_CHUNK)
+    msa.set_option(msa.OPT_ATTN_CHUNK, 512)
+    assert msa.get_option(msa.OPT_ATTN_CHUNK) == 512
+    msa.set_option(msa.OPT_ATTN_CHUNK, old)

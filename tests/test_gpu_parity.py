@@ -1,0 +1,255 @@
+"""GPU parity of libmsa against the CPU oracle, through the C ABI.
+
+Bar: block selections and the inverted index bit-exact; attention output
+within max-abs 1e-2 and relative L2 5e-3 of the fp64 oracle; lse within
+1e-3.  Inputs are seeded synthetic tensors (block_sparse_long_idx_amd.synth).
+Each stage is also fed the oracle's own upstream result, so no oracle input
+ever comes from the GPU path.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_long_idx_amd import msa
+from block_sparse_long_idx_amd.synth import (CONFIGS, bf16_bits, inputs_for,
+                                             make_decode_inputs,
+                                             make_prefill_inputs, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL_L2, LSE_ATOL = 1e-2, 5e-3, 1e-3
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def assert_attn_close(O, O_ref, lse=None, lse_ref=None):
+    O = np.asarray(O, dtype=np.float64)
+    err = np.abs(O - O_ref).max()
+    rel = np.linalg.norm(O - O_ref) / np.linalg.norm(O_ref)
+    assert np.isfinite(O).all()
+    assert err <= ATOL and rel <= RTOL_L2, (err, rel)
+    if lse is not None:
+        lerr = np.abs(np.asarray(lse, dtype=np.float64) - lse_ref).max()
+        assert lerr <= LSE_ATOL, lerr
+
+
+def _u16(t):
+    return {k: bf16_bits(v) for k, v in t.items()}
+
+
+def _dev(t):
+    return {k: v.cuda() for k, v in t.items()}
+
+
+# ----------------------------------------------------------------- stages
+STAGE_CASES = [
+    # N, H_q, H_kv, d_h, d_idx, k, n_hot, q_start, Nq
+    (1024, 4, 1, 64, 32, 4, 0, 0, 1024),        # the tiny workload
+    (1000, 8, 2, 128, 64, 4, 2, 0, 1000),       # ragged last block
+    (2000, 16, 4, 64, 128, 5, 3, 700, 1300),    # unaligned q_start
+    (5000, 6, 2, 128, 64, 32, 4, 0, 5000),      # k = 32, G = 3
+    (777, 2, 2, 64, 32, 1, 0, 0, 777),          # k = 1: local block only
+    (600, 64, 1, 128, 64, 3, 1, 0, 600),        # G = 64 (> 32 rows per position)
+]
+
+
+@pytest.mark.parametrize("case", STAGE_CASES, ids=lambda c: "N%d_Hq%d_Hkv%d_dh%d_di%d_k%d_qs%d" % (c[0], c[1], c[2], c[3], c[4], c[5], c[7]))
+def test_index_topk_stage(oracle_lib, case):
+    N, H_q, H_kv, d_h, d_idx, k, n_hot, q_start, Nq = case
+    say("index_topk", case)
+    t = make_prefill_inputs(N, H_q, H_kv, d_h, d_idx, n_hot=n_hot, seed=N + k)
+    u = _u16(t)
+    rows = np.arange(q_start, q_start + Nq)
+    ref = oracle_lib.select(u["q_idx"][rows], u["k_idx"], rows, k)
+    d = _dev(t)
+    for fused in (0,):
+        msa.set_option(msa.OPT_INDEX_FUSED, fused)
+        sel = msa.index_topk(d["q_idx"], d["k_idx"], k, q_start=q_start, Nq=Nq)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(sel.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("case", STAGE_CASES, ids=lambda c: "N%d_k%d_qs%d" % (c[0], c[5], c[7]))
+def test_invert_stage(oracle_lib, case):
+    N, H_q, H_kv, d_h, d_idx, k, n_hot, q_start, Nq = case
+    say("invert", case)
+    t = make_prefill_inputs(N, H_q, H_kv, d_h, d_idx, n_hot=n_hot, seed=N + k)
+    u = _u16(t)
+    rows = np.arange(q_start, q_start + Nq)
+    sel = oracle_lib.select(u["q_idx"][rows], u["k_idx"], rows, k)
+    nblk = (q_start + Nq + 127) // 128
+    rp, col, slot = oracle_lib.invert(sel, q_start, nblk)
+    g_rp, g_col, g_slot = msa.invert_index(torch.from_numpy(sel).cuda(), q_start=q_start)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(g_rp.cpu().numpy(), rp)
+    np.testing.assert_array_equal(g_col.cpu().numpy(), col)
+    np.testing.assert_array_equal(g_slot.cpu().numpy(), slot)
+
+
+@pytest.mark.parametrize("case", STAGE_CASES, ids=lambda c: "N%d_Hq%d_dh%d_k%d_qs%d" % (c[0], c[1], c[3], c[5], c[7]))
+def test_attn_stage(oracle_lib, case):
+    N, H_q, H_kv, d_h, d_idx, k, n_hot, q_start, Nq = case
+    say("attn", case)
+    t = make_prefill_inputs(N, H_q, H_kv, d_h, d_idx, n_hot=n_hot, seed=N + k)
+    u = _u16(t)
+    rows = np.arange(q_start, q_start + Nq)
+    scale = 1.0 / math.sqrt(d_h)
+    sel, O_ref, lse_ref = oracle_lib.prefill_rows(u, rows, k, scale)
+    nblk = (q_start + Nq + 127) // 128
+    rp, col, slot = oracle_lib.invert(sel, q_start, nblk)
+    d = _dev(t)
+    O, lse = msa.sparse_attn_fwd(
+        d["Q"], d["K"], d["V"], torch.from_numpy(rp.astype(np.int32)).cuda(),
+        torch.from_numpy(col.astype(np.int32)).cuda(),
+        torch.from_numpy(slot.astype(np.uint8)).cuda(), k, q_start=q_start, Nq=Nq,
+        scale=scale)
+    torch.cuda.synchronize()
+    assert_attn_close(O.cpu().numpy(), O_ref, lse.cpu().numpy(), lse_ref)
+
+
+# --------------------------------------------------------------- end to end
+E2E_CASES = [
+    # N, H_q, H_kv, d_h, d_idx, k, n_hot, chunk
+    (1024, 4, 1, 64, 32, 4, 0, 0),
+    (2000, 16, 4, 64, 128, 5, 3, 384),
+    (2000, 16, 4, 64, 128, 5, 3, 300),      # chunks not aligned to blocks
+    (3000, 8, 2, 128, 64, 8, 2, 1000),
+]
+
+
+@pytest.mark.parametrize("case", E2E_CASES, ids=lambda c: "N%d_k%d_chunk%d" % (c[0], c[5], c[7]))
+def test_prefill_end_to_end(oracle_lib, case):
+    N, H_q, H_kv, d_h, d_idx, k, n_hot, chunk = case
+    say("prefill", case)
+    t = make_prefill_inputs(N, H_q, H_kv, d_h, d_idx, n_hot=n_hot, seed=7 * N + k)
+    u = _u16(t)
+    rows = np.arange(N)
+    scale = 1.0 / math.sqrt(d_h)
+    sel_ref, O_ref, lse_ref = oracle_lib.prefill_rows(u, rows, k, scale)
+    d = _dev(t)
+    sel, O, lse = msa.prefill(d["Q"], d["K"], d["V"], d["q_idx"], d["k_idx"], k,
+                              scale=scale, chunk=chunk)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sel.cpu().numpy(), sel_ref)
+    assert_attn_close(O.cpu().numpy(), O_ref, lse.cpu().numpy(), lse_ref)
+
+
+def test_prefill_is_deterministic():
+    N, H_q, H_kv, d_h, d_idx, k = 3000, 16, 4, 128, 64, 8
+    say("determinism", N)
+    d = _dev(make_prefill_inputs(N, H_q, H_kv, d_h, d_idx, n_hot=3, seed=99))
+    outs = []
+    for _ in range(2):
+        outs.append(msa.prefill(d["Q"], d["K"], d["V"], d["q_idx"], d["k_idx"], k,
+                                chunk=1024))
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_prefill_chunking_does_not_change_results():
+    N, H_q, H_kv, d_h, d_idx, k = 2500, 8, 2, 64, 64, 6
+    say("chunk invariance", N)
+    d = _dev(make_prefill_inputs(N, H_q, H_kv, d_h, d_idx, n_hot=2, seed=5))
+    s1, O1, l1 = msa.prefill(d["Q"], d["K"], d["V"], d["q_idx"], d["k_idx"], k, chunk=0)
+    s2, O2, l2 = msa.prefill(d["Q"], d["K"], d["V"], d["q_idx"], d["k_idx"], k, chunk=640)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(O1, O2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------- decode
+DECODE_CASES = [
+    # B, N, H_q, H_kv, d_h, d_idx, k
+    (3, 5000, 16, 4, 128, 64, 8),
+    (2, 300, 8, 2, 64, 32, 4),          # fewer blocks than k
+    (2, 4096, 64, 4, 128, 64, 16),
+    (1, 129, 4, 1, 64, 128, 2),         # local block of one token
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "B%d_N%d_k%d" % (c[0], c[1], c[6]))
+def test_decode(oracle_lib, case):
+    B, N, H_q, H_kv, d_h, d_idx, k = case
+    say("decode", case)
+    t = make_decode_inputs(B, N, H_q, H_kv, d_h, d_idx, seed=N)
+    scale = 1.0 / math.sqrt(d_h)
+    d = _dev(t)
+    sel, O, lse = msa.decode(d["q"], d["q_idx"], d["K"], d["V"], d["k_idx"], k, scale=scale)
+    torch.cuda.synchronize()
+    sel, O, lse = sel.cpu().numpy(), O.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        u = {n: bf16_bits(t[n][b]) for n in t}
+        s_ref, O_ref, l_ref = oracle_lib.decode_one(u["q"], u["q_idx"], u["K"], u["V"],
+                                                    u["k_idx"], k, scale)
+        np.testing.assert_array_equal(sel[b], s_ref)
+        assert_attn_close(O[b], O_ref, lse[b], l_ref)
+
+
+# ------------------------------------------------------ full-size workloads
+def _full_prefill_check(oracle_lib, cfg, n_rows, attn_rows=None):
+    say("full prefill", cfg.name, "rows", n_rows)
+    t = inputs_for(cfg, device="cuda")
+    sel, O, lse = msa.prefill(t["Q"], t["K"], t["V"], t["q_idx"], t["k_idx"], cfg.k,
+                              scale=cfg.scale, chunk=cfg.chunk or 0)
+    torch.cuda.synchronize()
+    rows = np.array(sample_rows(cfg.N, n_rows))
+    rows_t = torch.from_numpy(rows).cuda()
+    k_idx = bf16_bits(t["k_idx"])
+    q_rows = bf16_bits(t["q_idx"][rows_t])
+    say("oracle select", len(rows))
+    sel_ref = oracle_lib.select(q_rows, k_idx, rows, cfg.k)
+    np.testing.assert_array_equal(sel[rows_t].cpu().numpy(), sel_ref)
+    arows = rows if attn_rows is None else np.array(sample_rows(cfg.N, attn_rows))
+    ar_t = torch.from_numpy(arows).cuda()
+    sel_a = sel_ref if attn_rows is None else \
+        oracle_lib.select(bf16_bits(t["q_idx"][ar_t]), k_idx, arows, cfg.k)
+    say("oracle attend", len(arows))
+    O_ref, lse_ref = oracle_lib.attend(bf16_bits(t["Q"][ar_t]), bf16_bits(t["K"]),
+                                       bf16_bits(t["V"]), sel_a, arows, cfg.scale)
+    assert_attn_close(O[ar_t].cpu().numpy(), O_ref, lse[ar_t].cpu().numpy(), lse_ref)
+    return t, sel
+
+
+def test_full_8k(oracle_lib):
+    cfg = CONFIGS["8k"]
+    t, sel = _full_prefill_check(oracle_lib, cfg, cfg.N, attn_rows=512)
+    # inverted index of the full selection, bit-exact
+    sel_np = sel.cpu().numpy()
+    rp, col, slot = oracle_lib.invert(sel_np, 0, cfg.nblk)
+    g_rp, g_col, g_slot = msa.invert_index(torch.from_numpy(sel_np).cuda())
+    np.testing.assert_array_equal(g_rp.cpu().numpy(), rp)
+    np.testing.assert_array_equal(g_col.cpu().numpy(), col)
+    np.testing.assert_array_equal(g_slot.cpu().numpy(), slot)
+
+
+def test_full_128k(oracle_lib):
+    _full_prefill_check(oracle_lib, CONFIGS["128k"], 512)
+
+
+@pytest.mark.slow
+def test_full_1m(oracle_lib):
+    _full_prefill_check(oracle_lib, CONFIGS["1m"], 256)
+
+
+@pytest.mark.slow
+def test_full_decode_1m(oracle_lib):
+    cfg = CONFIGS["decode_1m"]
+    say("full decode", cfg.name)
+    t = inputs_for(cfg, device="cuda")
+    sel, O, lse = msa.decode(t["q"], t["q_idx"], t["K"], t["V"], t["k_idx"], cfg.k,
+                             scale=cfg.scale)
+    torch.cuda.synchronize()
+    for b in (0, 13, 31):
+        say("oracle decode seq", b)
+        u = {n: bf16_bits(t[n][b]) for n in t}
+        s_ref, O_ref, l_ref = oracle_lib.decode_one(u["q"], u["q_idx"], u["K"], u["V"],
+                                                    u["k_idx"], cfg.k, cfg.scale)
+        np.testing.assert_array_equal(sel[b].cpu().numpy(), s_ref)
+        assert_attn_close(O[b].cpu().numpy(), O_ref, lse[b].cpu().numpy(), l_ref)
