@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""MSA forward benchmark on one MI355X.
+
+One step = the whole MSA prefill of a synthetic sequence (Index Branch,
+inverted index and KV-outer Main Branch over every query chunk), with all
+inputs resident in HBM.  Default workload: N = 1,048,576 tokens, 64 query
+heads, 4 KV heads, d_h 128, d_idx 64, k 16, B_k 128, query chunks of 65,536.
+
+Prints one JSON line: prefill tokens/s (value), effective TFLOP/s by the
+MSA FLOP formula 4*H_q*d_h*N*k*B_k + H_kv*d_idx*N^2 (as a fraction of the
+2.5 PFLOP/s bf16 MFMA peak), per-stage times, the roofline of the dominant
+kernel, the CPU oracle timed on sampled rows, and 128K-prefill and
+32 x 1M decode figures.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def formula_flops(cfg):
+    """MSA attention FLOPs: Main 4*H_q*d_h*N*k*B_k + Index H_kv*d_idx*N^2."""
+    main = 4.0 * cfg.H_q * cfg.d_h * cfg.N * cfg.k * cfg.B_k
+    index = float(cfg.H_kv) * cfg.d_idx * cfg.N * cfg.N
+    return main, index
+
+
+def chunks_of(cfg):
+    c = cfg.chunk or cfg.N
+    return [(q0, min(c, cfg.N - q0)) for q0 in range(0, cfg.N, c)]
+
+
+class Prefill:
+    """Preallocated buffers and the per-chunk call sequence of one step."""
+
+    def __init__(self, cfg, t):
+        import torch
+        from block_sparse_long_idx_amd import msa
+        self.cfg, self.t, self.msa = cfg, t, msa
+        dev = t["Q"].device
+        lib = msa.load()
+        self.chunks = chunks_of(cfg)
+        ws_i = ws_v = ws_a = nnz = 0
+        for q0, nq in self.chunks:
+            ws_i = max(ws_i, lib.msa_index_topk_workspace_bytes(q0, nq, cfg.H_kv, cfg.B_k, cfg.k))
+            ws_v = max(ws_v, lib.msa_invert_index_workspace_bytes(q0, nq, cfg.H_kv, cfg.B_k, cfg.k))
+            ws_a = max(ws_a, lib.msa_sparse_attn_fwd_workspace_bytes(
+                q0, nq, cfg.H_q, cfg.H_kv, cfg.d_h, cfg.B_k, cfg.k))
+            nnz = max(nnz, msa.selection_nnz(q0, nq, cfg.H_kv, cfg.k))
+        fused = msa.get_option(msa.OPT_INDEX_FUSED)
+        u8 = torch.uint8
+        self.ws_i = torch.empty(1 if fused else ws_i, dtype=u8, device=dev)
+        self.ws_v = torch.empty(ws_v, dtype=u8, device=dev)
+        self.ws_a = torch.empty(ws_a, dtype=u8, device=dev)
+        self.sel = torch.empty((cfg.N, cfg.H_kv, cfg.k), dtype=torch.int32, device=dev)
+        self.O = torch.empty((cfg.N, cfg.H_q, cfg.d_h), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((cfg.N, cfg.H_q), dtype=torch.float32, device=dev)
+        self.row_ptr = torch.empty(cfg.H_kv * cfg.nblk + 1, dtype=torch.int32, device=dev)
+        self.col = torch.empty(nnz, dtype=torch.int32, device=dev)
+        self.slot = torch.empty(nnz, dtype=torch.uint8, device=dev)
+        self.events = []
+
+    def step(self, record=False):
+        import torch
+        cfg, t, msa = self.cfg, self.t, self.msa
+        for q0, nq in self.chunks:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+            if record:
+                ev[0].record()
+            sel_c = self.sel[q0:q0 + nq]
+            msa.index_topk(t["q_idx"], t["k_idx"], cfg.k, q_start=q0, Nq=nq, sel=sel_c,
+                           ws=self.ws_i)
+            if record:
+                ev[1].record()
+            rp, col, slot = msa.invert_index(sel_c, q_start=q0, ws=self.ws_v,
+                                             row_ptr=self.row_ptr, col=self.col,
+                                             slot=self.slot)
+            if record:
+                ev[2].record()
+            msa.sparse_attn_fwd(t["Q"], t["K"], t["V"], rp, col, slot, cfg.k, q_start=q0,
+                                Nq=nq, scale=cfg.scale, O=self.O[q0:q0 + nq],
+                                lse=self.lse[q0:q0 + nq], ws=self.ws_a)
+            if record:
+                ev[3].record()
+                self.events.append(ev)
+
+    def stage_ms(self):
+        """Total ms per stage over the recorded steps' chunks."""
+        tot = [0.0, 0.0, 0.0]
+        for ev in self.events:
+            for s in range(3):
+                tot[s] += ev[s].elapsed_time(ev[s + 1])
+        return tot
+
+
+def time_prefill(cfg, t, steps, warmup):
+    import torch
+    pf = Prefill(cfg, t)
+    for _ in range(warmup):
+        pf.step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        pf.step(record=True)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    st = [x / steps for x in pf.stage_ms()]
+    return pf, ms, st
+
+
+def cpu_baseline(cfg, t, n_rows):
+    """The oracle, as it stands, on n_rows query rows spread over the sequence."""
+    import numpy as np
+    import torch
+    import oracle
+    from block_sparse_long_idx_amd.synth import bf16_bits, sample_rows
+    rows = np.array(sample_rows(cfg.N, n_rows))
+    rt = torch.from_numpy(rows).to(t["Q"].device)
+    k_idx, K, V = bf16_bits(t["k_idx"]), bf16_bits(t["K"]), bf16_bits(t["V"])
+    q_rows, Q_rows = bf16_bits(t["q_idx"][rt]), bf16_bits(t["Q"][rt])
+    oracle.build(force=False)
+    nthreads = oracle.threads()
+    t0 = time.perf_counter()
+    sel = oracle.select(q_rows, k_idx, rows, cfg.k, nthreads=nthreads)
+    oracle.attend(Q_rows, K, V, sel, rows, cfg.scale, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{len(rows)} query rows evenly spaced over positions 0..{cfg.N - 1} "
+                      f"of the same workload (all heads and groups), {dt:.1f} s wall"}
+
+
+def time_decode(cfg, steps, warmup):
+    import torch
+    from block_sparse_long_idx_amd import msa
+    from block_sparse_long_idx_amd.synth import inputs_for
+    t = inputs_for(cfg, device="cuda")
+    dev = t["q"].device
+    B, N = cfg.batch, cfg.N
+    ws = torch.empty(msa.decode_workspace_bytes(B, N, cfg.H_q, cfg.H_kv, cfg.d_h, cfg.k),
+                     dtype=torch.uint8, device=dev)
+    sel = torch.empty((B, cfg.H_kv, cfg.k), dtype=torch.int32, device=dev)
+    O = torch.empty((B, cfg.H_q, cfg.d_h), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, cfg.H_q), dtype=torch.float32, device=dev)
+
+    def one():
+        msa.decode(t["q"], t["q_idx"], t["K"], t["V"], t["k_idx"], cfg.k, scale=cfg.scale,
+                   sel=sel, O=O, lse=lse, ws=ws)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        one()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    nbytes = (B * N * cfg.H_kv * cfg.d_idx * 2                       # k_idx scan
+              + B * cfg.H_kv * cfg.k * cfg.B_k * cfg.d_h * 2 * 2      # selected K and V
+              + B * (cfg.H_q * cfg.d_h * 2 + cfg.H_kv * cfg.d_idx * 2)  # q, q_idx
+              + B * cfg.H_q * (cfg.d_h + 1) * 4)                      # O, lse
+    del t
+    return {"workload": f"decode B={B} x N={N}", "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(B / (ms / 1e3), 1),
+            "GB_per_s": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_per_step": nbytes}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="1m", choices=["tiny", "8k", "128k", "1m"])
+    ap.add_argument("--fused", type=int, default=1, help="fused Index-Branch kernel (1/0)")
+    ap.add_argument("--attn-chunk", type=int, default=0, help="positions per work item")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 128K and decode legs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_long_idx_amd import msa
+    from block_sparse_long_idx_amd.synth import CONFIGS, inputs_for
+    msa.load()
+    msa.set_option(msa.OPT_INDEX_FUSED, args.fused)
+    if args.attn_chunk:
+        msa.set_option(msa.OPT_ATTN_CHUNK, args.attn_chunk)
+    cfg = CONFIGS[args.workload]
+    log(f"[bench] workload {cfg.name}: generating inputs on the GPU")
+    t = inputs_for(cfg, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.warmup} warmup + {args.steps} steps")
+    pf, ms, stages = time_prefill(cfg, t, args.steps, args.warmup)
+    main_f, index_f = formula_flops(cfg)
+    tflops = (main_f + index_f) / (ms / 1e3) / 1e12
+    stage_names = ["index_topk", "invert_index", "sparse_attn_fwd"]
+    log(f"[bench] {ms:.2f} ms/step; stages " +
+        ", ".join(f"{n} {s:.2f} ms" for n, s in zip(stage_names, stages)))
+
+    # roofline of the dominant stage (the fused Index Branch is one kernel)
+    dom = max(range(3), key=lambda s: stages[s])
+    if dom == 0 and args.fused:
+        ach = index_f / (stages[0] / 1e3) / 1e12
+        roof = {"kernel": "index_topk_fused_kernel", "bound": "mfma",
+                "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "per_launch": f"{len(pf.chunks)} launches per step, one per query chunk; "
+                              "algorithmic flops = H_kv*d_idx*N^2 per step"}
+    else:
+        roof = {"kernel": stage_names[dom], "bound": "hbm", "achieved": None,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": None, "traffic": None}
+
+    out = {
+        "metric": "MSA prefill tokens/s + effective TFLOP/s (% bf16 MFMA peak) at 128K and 1M",
+        "value": round(cfg.N / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"MSA prefill N={cfg.N}", "N": cfg.N, "H_q": cfg.H_q,
+                   "H_kv": cfg.H_kv, "d_h": cfg.d_h, "d_idx": cfg.d_idx, "k": cfg.k,
+                   "B_k": cfg.B_k, "query_chunk": cfg.chunk or cfg.N,
+                   "index_variant": "fused" if args.fused else "two-kernel",
+                   "attn_chunk": msa.get_option(msa.OPT_ATTN_CHUNK)},
+        "effective_tflops": round(tflops, 2),
+        "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "formula_tflop_per_step": {"main": round(main_f / 1e12, 3),
+                                   "index": round(index_f / 1e12, 3)},
+        "stage_ms": {n: round(s, 3) for n, s in zip(stage_names, stages)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle on {args.cpu_rows} sampled rows")
+        out["cpu_baseline"] = cpu_baseline(cfg, t, args.cpu_rows)
+    del pf, t
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        extra = {}
+        if cfg.name != "128k":
+            c2 = CONFIGS["128k"]
+            log("[bench] 128K prefill leg")
+            t2 = inputs_for(c2, device="cuda")
+            _, ms2, st2 = time_prefill(c2, t2, max(3, args.steps), 1)
+            f2 = sum(formula_flops(c2))
+            extra["prefill_128k"] = {
+                "ms_per_step": round(ms2, 3), "tokens_per_s": round(c2.N / (ms2 / 1e3), 1),
+                "effective_tflops": round(f2 / (ms2 / 1e3) / 1e12, 2),
+                "frac_bf16_peak": round(f2 / (ms2 / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "stage_ms": {n: round(s, 3) for n, s in zip(stage_names, st2)}}
+            del t2
+            torch.cuda.empty_cache()
+        log("[bench] decode leg")
+        extra["decode_32x1m"] = time_decode(CONFIGS["decode_1m"], max(5, args.steps), 2)
+        torch.cuda.empty_cache()
+        out["extra"] = extra
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -37,18 +37,17 @@ __device__ __forceinline__ int kswz(int row) {
   return D == 32 ? ((row >> 1) & 3) : (row & 7);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void index_pool_kernel(
-    const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx,
-    int64_t q_start, int64_t Nq, int H_kv, int ntiles, float* __restrict__ P,
-    int64_t ldp) {
+// The sweep shared by both Index-Branch variants.  For every key block kb
+// it hands the pooled score of the lane's own query to `sink(kb, v)`; the
+// lane owns query q_own = qw0 + 32*h + n (lane half h <-> column group h).
+template <int D, typename Sink>
+__device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
+                                            const __bf16* __restrict__ k_idx, int64_t q_start,
+                                            int64_t Nq, int H_kv, int r, int tile,
+                                            __bf16 (*lds)[128 * D], Sink& sink) {
   constexpr int S = D / 16;   // MFMA k-steps
   constexpr int CH = D / 8;   // 16-byte chunks per key row
   constexpr int LOADS = 128 * CH / 256;
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][128 * D];
-
-  const int r = blockIdx.y;
-  const int tile = ntiles - 1 - (int)blockIdx.x;  // long rows first
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int h = lane >> 5, n = lane & 31;
@@ -92,12 +91,6 @@ __global__ __launch_bounds__(256) void index_pool_kernel(
     }
   };
 
-  // The lane owns one query for the output: half 0 -> column group 0.
-  const int64_t q_own = qw0 + 32 * h + n;
-  float* prow = P + ((int64_t)r * Nq + (q_own - q_start)) * ldp;
-  const bool own_ok = q_own < q_end;
-  float pend[4] = {0.f, 0.f, 0.f, 0.f};
-
   bf16x8 nxt[LOADS];
   if (kb_end > 0) {
     gload(0, nxt);
@@ -132,14 +125,106 @@ __global__ __launch_bounds__(256) void index_pool_kernel(
       }
       m0 = fmaxf(m0, __shfl_xor(m0, 32, kWave));
       m1 = fmaxf(m1, __shfl_xor(m1, 32, kWave));
-      pend[kb & 3] = h ? m1 : m0;
-      if (own_ok && ((kb & 3) == 3 || kb == kb_end_w - 1))
-        *reinterpret_cast<f32x4*>(prow + (kb & ~3)) =
-            f32x4{pend[0], pend[1], pend[2], pend[3]};
+      sink(kb, kb_end_w, h ? m1 : m0);
     }
     if (kb + 1 < kb_end) lstore(buf ^ 1, nxt);
     __syncthreads();
   }
+}
+
+// Sink of the two-kernel variant: stores the pooled scores, 4 blocks at a
+// time, into P[r][q - q_start][kb].
+struct PoolStore {
+  float* prow;
+  bool own_ok;
+  float pend[4];
+  __device__ __forceinline__ void operator()(int kb, int kb_end_w, float v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pend[e] = (kb & 3) == e ? v : pend[e];  // no dynamic index
+    if (own_ok && ((kb & 3) == 3 || kb == kb_end_w - 1))
+      *reinterpret_cast<f32x4*>(prow + (kb & ~3)) = f32x4{pend[0], pend[1], pend[2], pend[3]};
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void index_pool_kernel(
+    const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx,
+    int64_t q_start, int64_t Nq, int H_kv, int ntiles, float* __restrict__ P,
+    int64_t ldp) {
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2][128 * D];
+  const int r = blockIdx.y;
+  const int tile = ntiles - 1 - (int)blockIdx.x;  // long rows first
+  const int lane = threadIdx.x & 63;
+  const int64_t q_own = q_start + (int64_t)tile * 256 + (threadIdx.x >> 6) * 64 +
+                        32 * (lane >> 5) + (lane & 31);
+  PoolStore sink{P + ((int64_t)r * Nq + (q_own - q_start)) * ldp, q_own < q_start + Nq,
+                 {0.f, 0.f, 0.f, 0.f}};
+  index_sweep<D>(q_idx, k_idx, q_start, Nq, H_kv, r, tile, lds, sink);
+}
+
+// Sink of the fused variant: a running Top-LM list of (score, block) per
+// query, sorted by score, descending.  Blocks arrive in ascending order and
+// a new score must beat an equal one strictly, so among equal scores the
+// lower block stays ahead (ties go to the lower block index).
+template <int LM>
+struct TopkKeep {
+  int lb_own;
+  float sc[LM];
+  int bk[LM];
+  __device__ __forceinline__ void operator()(int kb, int, float v) {
+    if (kb < lb_own && v > sc[LM - 1]) {
+#pragma unroll
+      for (int j = LM - 1; j > 0; --j) {
+        const bool up = v > sc[j - 1];
+        const bool here = v > sc[j];
+        sc[j] = up ? sc[j - 1] : (here ? v : sc[j]);
+        bk[j] = up ? bk[j - 1] : (here ? kb : bk[j]);
+      }
+      if (v > sc[0]) {
+        sc[0] = v;
+        bk[0] = kb;
+      }
+    }
+  }
+};
+
+template <int D, int LM>
+__global__ __launch_bounds__(256) void index_topk_fused_kernel(
+    const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx, int64_t q_start,
+    int64_t Nq, int H_kv, int ntiles, int k, int32_t* __restrict__ sel) {
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2][128 * D];
+  const int r = blockIdx.y;
+  const int tile = ntiles - 1 - (int)blockIdx.x;  // long rows first
+  const int lane = threadIdx.x & 63;
+  const int64_t q_own = q_start + (int64_t)tile * 256 + (threadIdx.x >> 6) * 64 +
+                        32 * (lane >> 5) + (lane & 31);
+  const bool own_ok = q_own < q_start + Nq;
+  TopkKeep<LM> keep;
+  keep.lb_own = own_ok ? (int)(q_own / kBlock) : 0;
+#pragma unroll
+  for (int j = 0; j < LM; ++j) {
+    keep.sc[j] = -INFINITY;
+    keep.bk[j] = -1;
+  }
+  index_sweep<D>(q_idx, k_idx, q_start, Nq, H_kv, r, tile, lds, keep);
+  if (!own_ok) return;
+  int32_t* out = sel + ((q_own - q_start) * H_kv + r) * k;
+  const int K1 = k - 1, lb = keep.lb_own;
+  if (lb <= K1) {
+    for (int t = 0; t < k; ++t) out[t] = t <= lb ? t : -1;
+    return;
+  }
+  // the K1 best blocks in ascending order, then the local block (largest id)
+#pragma unroll
+  for (int j = 0; j < LM; ++j) {
+    if (j < K1) {
+      int rank = 0;
+#pragma unroll
+      for (int i = 0; i < LM; ++i) rank += (i < K1) & (keep.bk[i] < keep.bk[j]);
+      out[rank] = keep.bk[j];
+    }
+  }
+  out[K1] = lb;
 }
 
 hipError_t launch_index_pool(const void* q_idx, const void* k_idx, int64_t q_start,
@@ -267,9 +352,31 @@ hipError_t launch_topk_decode(const float* P, int64_t ldp, int B, int H_kv, int 
   return launch_topk(P, ldp, (int64_t)B * H_kv, 1, H_kv, 0, nblk, k, sel, stream);
 }
 
-hipError_t launch_index_topk_fused(const void*, const void*, int64_t, int64_t, int, int, int,
-                                   int32_t*, hipStream_t) {
-  return hipErrorNotSupported;
+template <int D>
+static void launch_fused_d(const __bf16* qi, const __bf16* ki, int64_t q_start, int64_t Nq,
+                           int H_kv, int k, int32_t* sel, hipStream_t stream) {
+  const int ntiles = (int)ceil_div(Nq, 256);
+  dim3 grid(ntiles, H_kv), block(256);
+  if (k <= 8)
+    index_topk_fused_kernel<D, 7><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
+  else if (k <= 16)
+    index_topk_fused_kernel<D, 15><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
+  else
+    index_topk_fused_kernel<D, 31><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
+}
+
+hipError_t launch_index_topk_fused(const void* q_idx, const void* k_idx, int64_t q_start,
+                                   int64_t Nq, int H_kv, int d_idx, int k, int32_t* sel,
+                                   hipStream_t stream) {
+  auto* qi = static_cast<const __bf16*>(q_idx);
+  auto* ki = static_cast<const __bf16*>(k_idx);
+  switch (d_idx) {
+    case 32: launch_fused_d<32>(qi, ki, q_start, Nq, H_kv, k, sel, stream); break;
+    case 64: launch_fused_d<64>(qi, ki, q_start, Nq, H_kv, k, sel, stream); break;
+    case 128: launch_fused_d<128>(qi, ki, q_start, Nq, H_kv, k, sel, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace msa

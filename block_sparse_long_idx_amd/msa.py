@@ -131,17 +131,23 @@ def index_topk(q_idx, k_idx, k, q_start=0, Nq=None, B_k=B_K, sel=None, ws=None):
     return sel
 
 
-def invert_index(sel, q_start=0, B_k=B_K, ws=None):
-    """Inverted index of sel [Nq, H_kv, k]: (row_ptr, col int32, slot uint8)."""
+def invert_index(sel, q_start=0, B_k=B_K, ws=None, row_ptr=None, col=None, slot=None):
+    """Inverted index of sel [Nq, H_kv, k]: (row_ptr, col int32, slot uint8).
+    Preallocated outputs may be passed (col/slot with >= nnz entries)."""
     _need_cuda(sel)
     Nq, H_kv, k = sel.shape
     lib = load()
     nblk = (q_start + Nq + B_k - 1) // B_k
     nnz = lib.msa_selection_nnz(q_start, Nq, H_kv, B_k, k)
     dev = sel.device
-    row_ptr = torch.empty(H_kv * nblk + 1, dtype=torch.int32, device=dev)
-    col = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
-    slot = torch.empty(max(nnz, 1), dtype=torch.uint8, device=dev)
+    if row_ptr is None:
+        row_ptr = torch.empty(H_kv * nblk + 1, dtype=torch.int32, device=dev)
+    if col is None:
+        col = torch.empty(max(nnz, 1), dtype=torch.int32, device=dev)
+    if slot is None:
+        slot = torch.empty(max(nnz, 1), dtype=torch.uint8, device=dev)
+    if row_ptr.numel() < H_kv * nblk + 1 or col.numel() < nnz or slot.numel() < nnz:
+        raise ValueError("preallocated inverted-index outputs are too small")
     need = lib.msa_invert_index_workspace_bytes(q_start, Nq, H_kv, B_k, k)
     if ws is None:
         ws = _workspace(need, dev)

@@ -68,11 +68,15 @@ def test_index_topk_stage(oracle_lib, case):
     rows = np.arange(q_start, q_start + Nq)
     ref = oracle_lib.select(u["q_idx"][rows], u["k_idx"], rows, k)
     d = _dev(t)
-    for fused in (0,):
-        msa.set_option(msa.OPT_INDEX_FUSED, fused)
-        sel = msa.index_topk(d["q_idx"], d["k_idx"], k, q_start=q_start, Nq=Nq)
-        torch.cuda.synchronize()
-        np.testing.assert_array_equal(sel.cpu().numpy(), ref)
+    old = msa.get_option(msa.OPT_INDEX_FUSED)
+    try:
+        for fused in (0, 1):
+            msa.set_option(msa.OPT_INDEX_FUSED, fused)
+            sel = msa.index_topk(d["q_idx"], d["k_idx"], k, q_start=q_start, Nq=Nq)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(sel.cpu().numpy(), ref, err_msg=f"fused={fused}")
+    finally:
+        msa.set_option(msa.OPT_INDEX_FUSED, old)
 
 
 @pytest.mark.parametrize("case", STAGE_CASES, ids=lambda c: "N%d_k%d_qs%d" % (c[0], c[5], c[7]))
@@ -123,10 +127,18 @@ E2E_CASES = [
 ]
 
 
+@pytest.fixture(params=[0, 1], ids=["twokernel", "fused"])
+def index_variant(request):
+    old = msa.get_option(msa.OPT_INDEX_FUSED)
+    msa.set_option(msa.OPT_INDEX_FUSED, request.param)
+    yield request.param
+    msa.set_option(msa.OPT_INDEX_FUSED, old)
+
+
 @pytest.mark.parametrize("case", E2E_CASES, ids=lambda c: "N%d_k%d_chunk%d" % (c[0], c[5], c[7]))
-def test_prefill_end_to_end(oracle_lib, case):
+def test_prefill_end_to_end(oracle_lib, case, index_variant):
     N, H_q, H_kv, d_h, d_idx, k, n_hot, chunk = case
-    say("prefill", case)
+    say("prefill", case, "fused", index_variant)
     t = make_prefill_inputs(N, H_q, H_kv, d_h, d_idx, n_hot=n_hot, seed=7 * N + k)
     u = _u16(t)
     rows = np.arange(N)
@@ -217,7 +229,7 @@ def _full_prefill_check(oracle_lib, cfg, n_rows, attn_rows=None):
     return t, sel
 
 
-def test_full_8k(oracle_lib):
+def test_full_8k(oracle_lib, index_variant):
     cfg = CONFIGS["8k"]
     t, sel = _full_prefill_check(oracle_lib, cfg, cfg.N, attn_rows=512)
     # inverted index of the full selection, bit-exact
@@ -229,7 +241,7 @@ def test_full_8k(oracle_lib):
     np.testing.assert_array_equal(g_slot.cpu().numpy(), slot)
 
 
-def test_full_128k(oracle_lib):
+def test_full_128k(oracle_lib, index_variant):
     _full_prefill_check(oracle_lib, CONFIGS["128k"], 512)
 
 
