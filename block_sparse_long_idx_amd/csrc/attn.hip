@@ -1,16 +1,28 @@
-// Main Branch, KV-outer ("MiniMax Sparse Attention" explainer, section 05
-// part 2): each KV block is loaded once per work item and the queries that
-// selected it are gathered through the inverted index; G heads x several
-// query positions are packed into one 128-row MFMA tile (query
-// concatenation); hot blocks are cut along the query dimension into work
-// items planned before launch (pre-scheduled chunking); each (query, head,
-// block) partial goes to a pre-assigned slot and a combine kernel merges
-// the slots through their log-sum-exp (two-phase forward).
+// Main Branch ("MiniMax Sparse Attention" explainer, section 05 part 2).
 //
-// Partial precision: non-local blocks store O_s in bf16 (the pages' IO
-// accounting is bf16) with lse_s in fp32; the local block -- the only one
-// with a causal mask and the only one for rows i < 128, where few tokens can
-// make |O| large -- is computed with a hi/lo split of P and stored in fp32.
+// KV-outer partial attention: each non-local KV block is loaded once per
+// work item and the queries that selected it are gathered through the
+// inverted index; G heads x several query positions are packed into MFMA
+// row tiles (query concatenation); hot blocks are cut along the query
+// dimension into work items planned before launch (pre-scheduled
+// chunking); each (query, head, block) partial goes to a pre-assigned slot
+// (two-phase forward).
+//
+// Combine: one work-group per (query block, group) loads that block's K/V,
+// computes the local block -- the query's own block, the only one with a
+// causal mask -- exactly on MFMA with a hi/lo split of P, and merges it with
+// the query's non-local partials through their log-sum-exp in ascending
+// slot (= block) order.  Keeping the local block out of the partial buffer
+// saves its round trip through HBM and keeps rows i < 128, which see only
+// their local block, in fp32 all the way.
+//
+// Partial precision: O_s in bf16 (the pages' IO accounting is bf16), lse_s
+// in fp32.  Workspace layouts (d_h = DH):
+//   Os    bf16 [Nq][k-1][DH/4][H_q][4]   non-local slot s of position iq
+//   lse_s fp32 [Nq][k-1][H_q]
+// Four consecutive d of consecutive heads are adjacent, so the 16 heads of
+// a position that one MFMA tile holds store 128 contiguous bytes per
+// instruction, and the combine reads them back the same way.
 #include "common.h"
 #include "msa_internal.h"
 
@@ -19,9 +31,9 @@ namespace msa {
 // ---------------------------------------------------------------------------
 // Work list.  Bucket (r, b) of the CSR holds first the queries whose local
 // block is b (positions inside block b, all of which select it), then the
-// queries that picked b as a non-local block.  Items: one "local" item for
-// the first part, then non-local items of at most `chunk` positions.
-// Item = {bucket, start offset into col, count, is_local}.
+// queries that picked b as a non-local block.  The first part is handled by
+// the combine; the second is cut into items of at most `chunk` positions.
+// Item = {bucket, start offset into col, count, 0}.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void bucket_items(int64_t bucket, const int32_t* row_ptr, int nblk,
                                              int64_t q_start, int64_t Nq, int chunk,
@@ -32,7 +44,7 @@ __device__ __forceinline__ void bucket_items(int64_t bucket, const int32_t* row_
   const int64_t hi = min(q_start + Nq, (int64_t)(b + 1) * kBlock);
   n_loc = hi > lo ? (int32_t)(hi - lo) : 0;
   n_non = cnt - n_loc;
-  items = (n_loc > 0) + (n_non + chunk - 1) / chunk;
+  items = (n_non + chunk - 1) / chunk;
 }
 
 __global__ __launch_bounds__(1024) void build_items_kernel(const int32_t* __restrict__ row_ptr,
@@ -62,187 +74,48 @@ __global__ __launch_bounds__(1024) void build_items_kernel(const int32_t* __rest
   for (int64_t x = lo; x < hi; ++x) {
     int32_t n_loc, n_non, it;
     bucket_items(x, row_ptr, nblk, q_start, Nq, chunk, n_loc, n_non, it);
-    int32_t start = row_ptr[x];
-    if (n_loc > 0) {
-      items[pos++] = make_int4((int)x, start, n_loc, 1);
-      start += n_loc;
-    }
-    for (int32_t done = 0; done < n_non; done += chunk) {
+    const int32_t start = row_ptr[x] + n_loc;
+    for (int32_t done = 0; done < n_non; done += chunk)
       items[pos++] = make_int4((int)x, start + done, min(chunk, n_non - done), 0);
-    }
   }
   if (t == 1023) *n_items = part[1023];
 }
 
 // ---------------------------------------------------------------------------
-// Partial attention of one work item.
+// Shared pieces.
 //
 // LDS: K block row-major [128][DH] (16-byte chunks XOR-swizzled by row) and
 // V block transposed [DH][128 + 4] (rows padded by 8 bytes, so the 32 rows a
 // wave reads at one key offset spread over the banks; the padding keeps
-// every V^T address a per-lane base plus a compile-time offset).
-// Each wave takes 32-row tiles; row R of the item = (position R / G, head
-// R % G of the group).  S^T = K . Q^T puts keys on MFMA rows so every lane
-// holds 16 keys of one row (row = lane % 32): the row max/sum are in-lane
-// plus one swap of lane halves.  O^T = V^T . P^T keeps the row on the lane,
-// so the 1/l normalisation is in-lane as well.
+// every V^T address a per-lane base plus a compile-time offset), plus the
+// item's query positions and slots.
+//
+// MFMA layout (v_mfma_f32_32x32x16_bf16): S^T = K . Q^T puts keys on the
+// rows, so each lane holds 16 keys of one tile row (row = lane % 32): row
+// max and sum are in-lane plus one swap of the lane halves.  O^T = V^T . P^T
+// keeps the row on the lane as well.  The d dimension of QK^T is permuted
+// identically on both operands (lane half h takes d in [h*DH/2,
+// (h+1)*DH/2)), which leaves the dot products unchanged.
 // ---------------------------------------------------------------------------
 constexpr int kVtPitch = kBlock + 4;  // elements per V^T row
+constexpr int kMaxItem = 2048;        // max query positions per work item
 
 template <int DH>
 struct AttnSmem {
   __bf16 k[kBlock * DH];
   __bf16 vt[DH * kVtPitch];
+  int32_t pos[kMaxItem];  // the item's query positions (its slice of col)
+  uint8_t sl[kMaxItem];   // and their slots
 };
 
 __device__ __forceinline__ int vt_off(int d, int key) { return d * kVtPitch + key; }
 
-// One 32-row tile of a work item (rows = (position, head) pairs).
-template <int DH, bool LOCAL>
-__device__ __forceinline__ void attn_tile(const AttnSmem<DH>& sm, const __bf16* __restrict__ Q,
-                                          const int32_t* __restrict__ col,
-                                          const uint8_t* __restrict__ slot, int start, int nrows,
-                                          int tile, int r, int G, int H_q, int k, int64_t key0,
-                                          int64_t q_start, float scale_log2,
-                                          __bf16* __restrict__ Os, float* __restrict__ lse_s,
-                                          float* __restrict__ Oloc, int h, int n) {
-  constexpr int S = DH / 16;    // k-steps of the QK^T MFMA chain
-  constexpr int NDG = DH / 32;  // 32-wide d groups of O
-  // ---- gather this lane's row: position, head, slot -------------------------
-  const int R = tile * 32 + n;
-  const bool row_ok = R < nrows;
-  int64_t pos = 0;
-  int hq = 0, sl = 0;
-  if (row_ok) {
-    const int p = R / G;
-    pos = col[start + p];
-    sl = slot[start + p];
-    hq = r * G + R % G;
-  }
-
-  // ---- S^T = K . Q^T: 4 groups of 32 keys ------------------------------------
-  f32x16 sacc[4];
-  {
-    bf16x8 qb[S];
-    const __bf16* qrow = Q + (pos * H_q + hq) * DH + (DH / 2) * h;
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-      qb[s] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + 8 * s) : bf16x8{};
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      sacc[g] = f32x16{};
-      const int krow = 32 * g + n;
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &sm.k[krow * DH + 8 * (((DH / 16) * h + s) ^ (krow & 7))]);
-        sacc[g] = mfma32(a, qb[s], sacc[g]);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // bound the LDS reads in flight
-    }
-  }
-
-  // ---- softmax over the block (scale folded into exp2) ---------------------
-  if (LOCAL) {
-    // key 32g + acc_row(j, h) is visible iff it is <= pos - key0; acc_row
-    // is 4h plus a constant, so compare the constant with a per-lane limit.
-    const int lim = (row_ok ? (int)(pos - key0) : kBlock - 1) - 4 * h;
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (32 * g + acc_row(j, 0) > lim) sacc[g][j] = -INFINITY;
-  }
-  float m = -INFINITY;
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) m = fmaxf(m, sacc[g][j]);
-  m = fmaxf(m, __shfl_xor(m, 32, kWave));
-  const float mb = m * scale_log2;
-
-  // ---- O^T = V^T . P^T, P formed one 16-key step at a time ----------------
-  // P^T operand of step (g, u): MFMA k-index 8h'+e is key 32g+16u+4h'+e
-  // (e < 4) or 32g+16u+8+4h'+(e-4), which is accumulator 8u+e of sacc[g].
-  f32x16 oacc[NDG];
-#pragma unroll
-  for (int dg = 0; dg < NDG; ++dg) oacc[dg] = f32x16{};
-  float l = 0.f;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      bf16x8 phi, plo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sacc[g][8 * u + e] * scale_log2 - mb);
-        l += p;
-        phi[e] = f2bf(p);
-        if (LOCAL) plo[e] = f2bf(p - bf2f(phi[e]));
-      }
-      const int kb0 = 32 * g + 16 * u + 4 * h;
-#pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) {
-        const int d = 32 * dg + n;
-        const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(&sm.vt[vt_off(d, kb0)]);
-        const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(&sm.vt[vt_off(d, kb0 + 8)]);
-        const bf16x8 a = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        oacc[dg] = mfma32(a, phi, oacc[dg]);
-        if (LOCAL) oacc[dg] = mfma32(a, plo, oacc[dg]);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  l += __shfl_xor(l, 32, kWave);
-
-  // ---- write the partial ----------------------------------------------------
-  if (!row_ok) return;
-  const float inv = 1.f / l;
-  const int64_t iq = pos - q_start;
-  if (LOCAL) {
-    float* dst = Oloc + (iq * H_q + hq) * DH;
-#pragma unroll
-    for (int dg = 0; dg < NDG; ++dg)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        *reinterpret_cast<f32x4*>(dst + 32 * dg + 8 * qd + 4 * h) =
-            f32x4{oacc[dg][4 * qd] * inv, oacc[dg][4 * qd + 1] * inv,
-                  oacc[dg][4 * qd + 2] * inv, oacc[dg][4 * qd + 3] * inv};
-  } else {
-    __bf16* dst = Os + ((iq * (k - 1) + sl) * H_q + hq) * DH;
-#pragma unroll
-    for (int dg = 0; dg < NDG; ++dg)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        *reinterpret_cast<bf16x4*>(dst + 32 * dg + 8 * qd + 4 * h) =
-            bf16x4{f2bf(oacc[dg][4 * qd] * inv), f2bf(oacc[dg][4 * qd + 1] * inv),
-                   f2bf(oacc[dg][4 * qd + 2] * inv), f2bf(oacc[dg][4 * qd + 3] * inv)};
-  }
-  if (h == 0) lse_s[(iq * k + sl) * H_q + hq] = (mb + log2f(l)) * 0.69314718055994531f;
-}
-
+// K and V of block (group r, keys key0..key0+127); keys >= Nk read as 0.
 template <int DH>
-__global__ __launch_bounds__(256, 2) void attn_kv_outer_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const int32_t* __restrict__ col, const uint8_t* __restrict__ slot,
-    const int4* __restrict__ items, const int32_t* __restrict__ n_items, int64_t q_start,
-    int64_t Nk, int H_q, int H_kv, int G, int nblk, int k, float scale_log2,
-    __bf16* __restrict__ Os, float* __restrict__ lse_s, float* __restrict__ Oloc) {
+__device__ __forceinline__ void stage_kv(AttnSmem<DH>& sm, const __bf16* __restrict__ K,
+                                         const __bf16* __restrict__ V, int r, int H_kv,
+                                         int64_t key0, int64_t Nk, int t) {
   constexpr int CH = DH / 8;  // 16-byte chunks per K row
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  AttnSmem<DH>& sm = *reinterpret_cast<AttnSmem<DH>*>(smem_raw);
-
-  const int item_id = blockIdx.x;
-  if (item_id >= *n_items) return;
-  const int4 it = items[item_id];
-  const int bucket = it.x, start = it.y, count = it.z;
-  const bool local = it.w != 0;
-  const int r = bucket / nblk, b = bucket % nblk;
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int h = lane >> 5, n = lane & 31;
-  const int64_t key0 = (int64_t)b * kBlock;
-
-  // ---- stage K (row-major, swizzled) and V^T --------------------------------
   for (int id = t; id < kBlock * CH; id += 256) {
     const int row = id / CH, c = id % CH;
     bf16x8 v = {};
@@ -265,83 +138,360 @@ __global__ __launch_bounds__(256, 2) void attn_kv_outer_kernel(
       *reinterpret_cast<bf16x4*>(&sm.vt[vt_off(8 * c + e, 4 * kq)]) = w;
     }
   }
-  __syncthreads();
+}
 
-  const int nrows = count * G;
-  const int ntile = (nrows + 31) / 32;
-  for (int tile = wave; tile < ntile; tile += 4) {
-    if (local)
-      attn_tile<DH, true>(sm, Q, col, slot, start, nrows, tile, r, G, H_q, k, key0, q_start,
-                          scale_log2, Os, lse_s, Oloc, h, n);
-    else
-      attn_tile<DH, false>(sm, Q, col, slot, start, nrows, tile, r, G, H_q, k, key0, q_start,
-                           scale_log2, Os, lse_s, Oloc, h, n);
+// Row of a 32-row tile held by this lane: item row R = tile*32 + n is
+// (position R / G of the item, head R % G of the group).
+struct TileRow {
+  int pos;  // absolute query position (< 2^31)
+  int hq, sl;
+  bool ok;
+};
+
+template <int DH>
+__device__ __forceinline__ TileRow tile_row(const AttnSmem<DH>& sm, int nrows, int tile, int r,
+                                            int G, int n) {
+  TileRow t{0, 0, 0, false};
+  const int R = tile * 32 + n;
+  if (R < nrows) {
+    const int p = R / G;
+    t.pos = sm.pos[p];
+    t.sl = sm.sl[p];
+    t.hq = r * G + R % G;
+    t.ok = true;
   }
+  return t;
+}
+
+// Q operand of the lane's row (MFMA B: 16 d x 32 rows per k-step).  Rows
+// past the item's end read row 0 of Q instead (always valid memory): a row
+// only feeds its own MFMA column, and such rows are never stored.
+template <int DH>
+__device__ __forceinline__ void load_q(bf16x8 (&qb)[DH / 16], const __bf16* __restrict__ Q,
+                                       const TileRow& t, int H_q, int h) {
+  const __bf16* qrow = Q + ((int64_t)t.pos * H_q + t.hq) * DH + (DH / 2) * h;
+#pragma unroll
+  for (int s = 0; s < DH / 16; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + 8 * s);
+}
+
+// K fragment (MFMA A: 32 keys x 16 d) of key group g, k-step s.
+template <int DH>
+__device__ __forceinline__ bf16x8 k_frag(const AttnSmem<DH>& sm, int g, int s, int h, int n) {
+  const int krow = 32 * g + n;
+  return *reinterpret_cast<const bf16x8*>(
+      &sm.k[krow * DH + 8 * (((DH / 16) * h + s) ^ (krow & 7))]);
+}
+
+// V^T fragment (MFMA A: 32 d x 16 keys) for d = 32*dg + n and the keys of
+// P^T step (g, u): MFMA k-index 8h'+e is key 32g+16u+4h'+e (e < 4) or
+// 32g+16u+8+4h'+(e-4), which is accumulator 8u+e of the S^T group g.
+template <int DH>
+__device__ __forceinline__ bf16x8 v_frag(const AttnSmem<DH>& sm, int dg, int g, int u, int h,
+                                         int n) {
+  const int d = 32 * dg + n, kb0 = 32 * g + 16 * u + 4 * h;
+  const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(&sm.vt[vt_off(d, kb0)]);
+  const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(&sm.vt[vt_off(d, kb0 + 8)]);
+  return bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
 }
 
 // ---------------------------------------------------------------------------
-// Combine: for each (position, head) merge its n_sel = min(k, lb+1) partials
-// in ascending slot order (= ascending block; the local block is last):
-//   M = max lse_s, w_s = exp(lse_s - M), O = sum w_s O_s / sum w_s,
-//   lse = M + ln sum w_s.
-// One work-group per position; 4 threads per head, DH/4 dims each.
+// KV-outer partial attention of non-local work items.  64-row tiles per
+// wave, as two 32-row halves c = 0, 1 that share every K and V^T fragment
+// read from LDS (each fragment feeds two MFMAs).  P is kept in bf16
+// registers and O is produced in halves of d so the accumulators fit two
+// waves per SIMD.  The next tile's Q rows are fetched into the Q registers
+// once the softmax is done, overlapping the gather with PV and the stores.
 // ---------------------------------------------------------------------------
 template <int DH>
-__global__ __launch_bounds__(256) void combine_kernel(const __bf16* __restrict__ Os,
-                                                      const float* __restrict__ lse_s,
-                                                      const float* __restrict__ Oloc,
-                                                      int64_t q_start, int H_q, int k,
-                                                      float* __restrict__ O,
-                                                      float* __restrict__ lse) {
-  constexpr int DQ = DH / 4;
-  const int64_t iq = blockIdx.x;
-  const int64_t i = q_start + iq;
-  const int n_sel = (int)min((int64_t)k, i / kBlock + 1);
-  for (int hq = threadIdx.x / 4; hq < H_q; hq += 64) {
-    const int d0 = (threadIdx.x & 3) * DQ;
-    const float* ls = lse_s + iq * k * H_q + hq;
-    float M = -INFINITY;
-    for (int s = 0; s < n_sel; ++s) M = fmaxf(M, ls[(int64_t)s * H_q]);
-    float acc[DQ];
+__device__ __forceinline__ void attn_item(const AttnSmem<DH>& sm, const __bf16* __restrict__ Q,
+                                          int nrows, int wave, int r, int G, int H_q, int k,
+                                          int64_t q_start, float scale_log2,
+                                          __bf16* __restrict__ Os, float* __restrict__ lse_s,
+                                          int h, int n) {
+  constexpr int S = DH / 16;
+  constexpr int NDG = DH / 32;
+  const int ntile = (nrows + 63) / 64;
+  if (wave >= ntile) return;
+  TileRow row[2];
+  bf16x8 qb[2][S];
 #pragma unroll
-    for (int d = 0; d < DQ; ++d) acc[d] = 0.f;
-    float den = 0.f;
-    for (int s = 0; s < n_sel - 1; ++s) {
-      const float w = __expf(ls[(int64_t)s * H_q] - M);
-      den += w;
-      const __bf16* src = Os + ((iq * (k - 1) + s) * H_q + hq) * DH + d0;
+  for (int c = 0; c < 2; ++c) {
+    row[c] = tile_row<DH>(sm, nrows, 2 * wave + c, r, G, n);
+    load_q<DH>(qb[c], Q, row[c], H_q, h);
+  }
+  for (int tile = wave; tile < ntile; tile += 4) {
+    // ---- S^T = K . Q^T for both halves ----------------------------------------
+    f32x16 sacc[2][4];
 #pragma unroll
-      for (int v = 0; v < DQ / 8; ++v) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + 8 * v);
+    for (int g0 = 0; g0 < 4; g0 += 2) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[8 * v + e] += w * bf2f(x[e]);
+      for (int c = 0; c < 2; ++c) sacc[c][g0] = sacc[c][g0 + 1] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+#pragma unroll
+        for (int g = g0; g < g0 + 2; ++g) {
+          const bf16x8 a = k_frag<DH>(sm, g, s, h, n);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) sacc[c][g] = mfma32(a, qb[c][s], sacc[c][g]);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    {
-      const float w = __expf(ls[(int64_t)(n_sel - 1) * H_q] - M);
-      den += w;
-      const float* src = Oloc + (iq * H_q + hq) * DH + d0;
+    // ---- softmax: P in bf16, row sums l ---------------------------------------
+    bf16x8 pb[2][4][2];
+    float mb[2], l[2];
 #pragma unroll
-      for (int v = 0; v < DQ / 4; ++v) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * v);
+    for (int c = 0; c < 2; ++c) {
+      float m = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * v + e] += w * x[e];
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) m = fmaxf(m, sacc[c][g][j]);
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      mb[c] = m * scale_log2;
+      float ls = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(sacc[c][g][8 * u + e] * scale_log2 - mb[c]);
+            ls += p;
+            pb[c][g][u][e] = f2bf(p);
+          }
+      l[c] = ls + __shfl_xor(ls, 32, kWave);
+    }
+    // ---- prefetch the next tile's Q into qb -----------------------------------
+    TileRow nrow[2] = {{0, 0, 0, false}, {0, 0, 0, false}};
+    if (tile + 4 < ntile) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) nrow[c] = tile_row<DH>(sm, nrows, 2 * (tile + 4) + c, r, G, n);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) load_q<DH>(qb[c], Q, nrow[c], H_q, h);
+    // ---- O^T = V^T . P^T in halves of d, stored as bf16 partials -------------
+#pragma unroll
+    for (int half = 0; half < NDG / 2; ++half) {
+      f32x16 oacc[2][2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) oacc[c][0] = oacc[c][1] = f32x16{};
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+#pragma unroll
+          for (int dd = 0; dd < 2; ++dd) {
+            const bf16x8 a = v_frag<DH>(sm, 2 * half + dd, g, u, h, n);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) oacc[c][dd] = mfma32(a, pb[c][g][u], oacc[c][dd]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    const float inv = 1.f / den;
-    float* dst = O + (iq * H_q + hq) * DH + d0;
 #pragma unroll
-    for (int v = 0; v < DQ / 4; ++v)
-      *reinterpret_cast<f32x4*>(dst + 4 * v) =
-          f32x4{acc[4 * v] * inv, acc[4 * v + 1] * inv, acc[4 * v + 2] * inv,
-                acc[4 * v + 3] * inv};
-    if (lse && (threadIdx.x & 3) == 0) lse[iq * H_q + hq] = M + __logf(den);
+      for (int c = 0; c < 2; ++c) {
+        if (!row[c].ok) continue;
+        const float inv = 1.f / l[c];
+        const int iq = row[c].pos - (int)q_start;
+        // d = 32dg + 8qd + 4h + e  ->  group of four dq = 8dg + 2qd + h
+        __bf16* dst = Os + (int64_t)(iq * (k - 1) + row[c].sl) * (DH / 4) * H_q * 4 +
+                      row[c].hq * 4;
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<bf16x4*>(dst + (8 * (2 * half + dd) + 2 * qd + h) * H_q * 4) =
+                bf16x4{f2bf(oacc[c][dd][4 * qd] * inv), f2bf(oacc[c][dd][4 * qd + 1] * inv),
+                       f2bf(oacc[c][dd][4 * qd + 2] * inv), f2bf(oacc[c][dd][4 * qd + 3] * inv)};
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one half's accumulators live at a time
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      if (row[c].ok && h == 0)
+        lse_s[(int64_t)((row[c].pos - (int)q_start) * (k - 1) + row[c].sl) * H_q + row[c].hq] =
+            (mb[c] + log2f(l[c])) * 0.69314718055994531f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) row[c] = nrow[c];
   }
 }
 
-int64_t attn_max_items(int64_t nb, int64_t nnz, int chunk) {
-  return 2 * nb + nnz / chunk + 1;
+template <int DH>
+__global__ __launch_bounds__(256, 2) void attn_kv_outer_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const int32_t* __restrict__ col, const uint8_t* __restrict__ slot,
+    const int4* __restrict__ items, const int32_t* __restrict__ n_items, int64_t q_start,
+    int64_t Nk, int H_q, int H_kv, int G, int nblk, int k, float scale_log2,
+    __bf16* __restrict__ Os, float* __restrict__ lse_s) {
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  AttnSmem<DH>& sm = *reinterpret_cast<AttnSmem<DH>*>(smem_raw);
+  const int item_id = blockIdx.x;
+  if (item_id >= *n_items) return;
+  const int4 it = items[item_id];
+  const int bucket = it.x, start = it.y, count = it.z;
+  const int r = bucket / nblk, b = bucket % nblk;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  for (int p = t; p < count; p += 256) {
+    sm.pos[p] = col[start + p];
+    sm.sl[p] = slot[start + p];
+  }
+  stage_kv<DH>(sm, K, V, r, H_kv, (int64_t)b * kBlock, Nk, t);
+  __syncthreads();
+  attn_item<DH>(sm, Q, count * G, wave, r, G, H_q, k, q_start, scale_log2, Os, lse_s,
+                lane >> 5, lane & 31);
 }
+
+// ---------------------------------------------------------------------------
+// Combine with the local block.  Work-group = (query block b, group r): the
+// chunk's positions inside block b, times the G heads of group r, in 32-row
+// tiles.  Per tile: S^T over the block with the causal mask key <= i, P
+// split as hi + lo bf16 (two MFMAs, ~fp32 accuracy), O_loc and lse_loc in
+// registers; then the row's non-local partials (slots 0 .. n_sel-2) and the
+// local block (slot n_sel-1) are merged in ascending slot order:
+//   M = max lse, w_s = exp(lse_s - M), O = sum w_s O_s / sum w_s,
+//   lse = M + ln sum w_s.
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(256, 2) void combine_local_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    int64_t q_start, int64_t Nq, int64_t Nk, int H_q, int H_kv, int G, int k,
+    float scale_log2, const __bf16* __restrict__ Os, const float* __restrict__ lse_s,
+    float* __restrict__ O, float* __restrict__ lse) {
+  constexpr int S = DH / 16;
+  constexpr int NDG = DH / 32;
+  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+  AttnSmem<DH>& sm = *reinterpret_cast<AttnSmem<DH>*>(smem_raw);
+  const int r = blockIdx.y;
+  const int64_t b = q_start / kBlock + blockIdx.x;
+  const int64_t p0 = max(q_start, b * kBlock), p1 = min(q_start + Nq, (b + 1) * kBlock);
+  const int npos = (int)(p1 - p0);
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int h = lane >> 5, n = lane & 31;
+  const int n_sel = (int)min((int64_t)k, b + 1);
+  for (int p = t; p < npos; p += 256) {
+    sm.pos[p] = (int)(p0 + p);
+    sm.sl[p] = 0;
+  }
+  const int64_t key0 = b * kBlock;
+  stage_kv<DH>(sm, K, V, r, H_kv, key0, Nk, t);
+  __syncthreads();
+
+  const int nrows = npos * G;
+  const int ntile = (nrows + 31) / 32;
+  for (int tile = wave; tile < ntile; tile += 4) {
+    const TileRow row = tile_row<DH>(sm, nrows, tile, r, G, n);
+    // ---- local block: S^T with the causal mask --------------------------------
+    f32x16 sacc[4];
+    {
+      bf16x8 qb[S];
+      load_q<DH>(qb, Q, row, H_q, h);
+#pragma unroll
+      for (int g0 = 0; g0 < 4; g0 += 2) {
+        sacc[g0] = sacc[g0 + 1] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+          for (int g = g0; g < g0 + 2; ++g)
+            sacc[g] = mfma32(k_frag<DH>(sm, g, s, h, n), qb[s], sacc[g]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // key 32g + acc_row(j, h) is visible iff it is <= pos - key0; acc_row
+    // is 4h plus a constant, so compare the constant with a per-lane limit.
+    const int lim = (row.ok ? (int)(row.pos - key0) : kBlock - 1) - 4 * h;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (32 * g + acc_row(j, 0) > lim) sacc[g][j] = -INFINITY;
+    float m = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) m = fmaxf(m, sacc[g][j]);
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    const float mb = m * scale_log2;
+    f32x16 oacc[NDG];
+#pragma unroll
+    for (int dg = 0; dg < NDG; ++dg) oacc[dg] = f32x16{};
+    float l = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 phi, plo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(sacc[g][8 * u + e] * scale_log2 - mb);
+          l += p;
+          phi[e] = f2bf(p);
+          plo[e] = f2bf(p - bf2f(phi[e]));
+        }
+#pragma unroll
+        for (int dg = 0; dg < NDG; ++dg) {
+          const bf16x8 a = v_frag<DH>(sm, dg, g, u, h, n);
+          oacc[dg] = mfma32(a, phi, oacc[dg]);
+          oacc[dg] = mfma32(a, plo, oacc[dg]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += __shfl_xor(l, 32, kWave);
+    if (!row.ok) continue;
+
+    // ---- merge with the non-local partials ------------------------------------
+    const int iq = row.pos - (int)q_start;
+    const float lse_loc = (mb + log2f(l)) * 0.69314718055994531f;
+    const float* ls = lse_s + (int64_t)iq * (k - 1) * H_q + row.hq;
+    float M = lse_loc;
+    for (int s = 0; s < n_sel - 1; ++s) M = fmaxf(M, ls[s * H_q]);
+    float acc[NDG][16];
+#pragma unroll
+    for (int dg = 0; dg < NDG; ++dg)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[dg][j] = 0.f;
+    float den = 0.f;
+    const __bf16* src = Os + (int64_t)iq * (k - 1) * (DH / 4) * H_q * 4 + row.hq * 4;
+    for (int s = 0; s < n_sel - 1; ++s) {
+      const float w = __expf(ls[s * H_q] - M);
+      den += w;
+      const __bf16* ps = src + (int64_t)s * (DH / 4) * H_q * 4;
+      bf16x4 x[NDG][4];
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          x[dg][qd] = *reinterpret_cast<const bf16x4*>(ps + (8 * dg + 2 * qd + h) * H_q * 4);
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[dg][4 * qd + e] += w * bf2f(x[dg][qd][e]);
+    }
+    const float w_loc = __expf(lse_loc - M);  // local slot, last
+    den += w_loc;
+    const float wl = w_loc / l;               // O_loc = oacc / l
+    const float inv = 1.f / den;
+    float* dst = O + ((int64_t)iq * H_q + row.hq) * DH;
+#pragma unroll
+    for (int dg = 0; dg < NDG; ++dg)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = (acc[dg][4 * qd + e] + wl * oacc[dg][4 * qd + e]) * inv;
+        *reinterpret_cast<f32x4*>(dst + 32 * dg + 8 * qd + 4 * h) = o;
+      }
+    if (lse && h == 0) lse[(int64_t)iq * H_q + row.hq] = M + __logf(den);
+  }
+}
+
+int attn_max_chunk() { return kMaxItem; }
+
+int64_t attn_max_items(int64_t nb, int64_t nnz, int chunk) { return nb + nnz / chunk + 1; }
 
 hipError_t launch_build_items(const int32_t* row_ptr, int64_t nb, int nblk, int64_t q_start,
                               int64_t Nq, int chunk, int4* items, int32_t* n_items,
@@ -351,18 +501,21 @@ hipError_t launch_build_items(const int32_t* row_ptr, int64_t nb, int nblk, int6
   return hipGetLastError();
 }
 
+template <typename Kern>
+static hipError_t allow_lds(Kern* kern, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 static bool attn_lds_ready = false;
 
-hipError_t attn_prepare() {
-  // The d_h = 128 kernel needs a little over 64 KiB of LDS per work-group.
+static hipError_t attn_prepare() {
+  // The d_h = 128 kernels need more than 64 KiB of LDS per work-group.
   if (attn_lds_ready) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kv_outer_kernel<128>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)sizeof(AttnSmem<128>));
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kv_outer_kernel<64>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)sizeof(AttnSmem<64>));
+  hipError_t e = allow_lds(&attn_kv_outer_kernel<128>, sizeof(AttnSmem<128>));
+  if (e == hipSuccess) e = allow_lds(&attn_kv_outer_kernel<64>, sizeof(AttnSmem<64>));
+  if (e == hipSuccess) e = allow_lds(&combine_local_kernel<128>, sizeof(AttnSmem<128>));
+  if (e == hipSuccess) e = allow_lds(&combine_local_kernel<64>, sizeof(AttnSmem<64>));
   if (e == hipSuccess) attn_lds_ready = true;
   return e;
 }
@@ -371,9 +524,10 @@ hipError_t launch_attn(const void* Q, const void* K, const void* V, const int32_
                        const uint8_t* slot, const int4* items, const int32_t* n_items,
                        int64_t max_items, int64_t q_start, int64_t Nk, int H_q, int H_kv,
                        int d_h, int nblk, int k, float scale, void* Os, float* lse_s,
-                       float* Oloc, hipStream_t stream) {
+                       hipStream_t stream) {
   hipError_t e = attn_prepare();
   if (e != hipSuccess) return e;
+  if (k < 2) return hipSuccess;  // no non-local blocks
   const int G = H_q / H_kv;
   const float scale_log2 = scale * 1.4426950408889634f;
   auto* q = static_cast<const __bf16*>(Q);
@@ -382,28 +536,38 @@ hipError_t launch_attn(const void* Q, const void* K, const void* V, const int32_
   auto* os = static_cast<__bf16*>(Os);
   dim3 grid((unsigned)max_items), block(256);
   if (d_h == 128)
-    attn_kv_outer_kernel<128><<<grid, block, sizeof(AttnSmem<128>), stream>>>(q, kk, v, col, slot, items, n_items,
-                                                          q_start, Nk, H_q, H_kv, G, nblk, k,
-                                                          scale_log2, os, lse_s, Oloc);
+    attn_kv_outer_kernel<128><<<grid, block, sizeof(AttnSmem<128>), stream>>>(
+        q, kk, v, col, slot, items, n_items, q_start, Nk, H_q, H_kv, G, nblk, k, scale_log2, os,
+        lse_s);
   else if (d_h == 64)
-    attn_kv_outer_kernel<64><<<grid, block, sizeof(AttnSmem<64>), stream>>>(q, kk, v, col, slot, items, n_items,
-                                                         q_start, Nk, H_q, H_kv, G, nblk, k,
-                                                         scale_log2, os, lse_s, Oloc);
+    attn_kv_outer_kernel<64><<<grid, block, sizeof(AttnSmem<64>), stream>>>(
+        q, kk, v, col, slot, items, n_items, q_start, Nk, H_q, H_kv, G, nblk, k, scale_log2, os,
+        lse_s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const void* Os, const float* lse_s, const float* Oloc,
-                          int64_t q_start, int64_t Nq, int H_q, int d_h, int k, float* O,
-                          float* lse, hipStream_t stream) {
+hipError_t launch_combine(const void* Q, const void* K, const void* V, const void* Os,
+                          const float* lse_s, int64_t q_start, int64_t Nq, int64_t Nk, int H_q,
+                          int H_kv, int d_h, int k, float scale, float* O, float* lse,
+                          hipStream_t stream) {
+  hipError_t e = attn_prepare();
+  if (e != hipSuccess) return e;
+  const int G = H_q / H_kv;
+  const float scale_log2 = scale * 1.4426950408889634f;
+  const int64_t nqb = (q_start + Nq - 1) / kBlock - q_start / kBlock + 1;
+  dim3 grid((unsigned)nqb, H_kv), block(256);
+  auto* q = static_cast<const __bf16*>(Q);
+  auto* kk = static_cast<const __bf16*>(K);
+  auto* v = static_cast<const __bf16*>(V);
   auto* os = static_cast<const __bf16*>(Os);
   if (d_h == 128)
-    combine_kernel<128><<<(unsigned)Nq, 256, 0, stream>>>(os, lse_s, Oloc, q_start, H_q, k, O,
-                                                          lse);
+    combine_local_kernel<128><<<grid, block, sizeof(AttnSmem<128>), stream>>>(
+        q, kk, v, q_start, Nq, Nk, H_q, H_kv, G, k, scale_log2, os, lse_s, O, lse);
   else if (d_h == 64)
-    combine_kernel<64><<<(unsigned)Nq, 256, 0, stream>>>(os, lse_s, Oloc, q_start, H_q, k, O,
-                                                         lse);
+    combine_local_kernel<64><<<grid, block, sizeof(AttnSmem<64>), stream>>>(
+        q, kk, v, q_start, Nq, Nk, H_q, H_kv, G, k, scale_log2, os, lse_s, O, lse);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

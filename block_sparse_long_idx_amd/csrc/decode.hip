@@ -15,46 +15,67 @@
 
 namespace msa {
 
-// (1) Each lane owns one (token, group) pair of 16 consecutive tokens and
-// computes its full d_idx-long dot product; lanes of the same group then
-// max-reduce.  Requires H_kv | 64.  Only blocks before the local block.
+// (1) Split scan.  A wavefront streams one 128-token block at a time as
+// contiguous 1 KiB loads (lane l takes elements 8l..8l+7 of every KiB), so
+// each load instruction is fully coalesced.  Those 8 values belong to one
+// (token, group) segment of D values held by D/8 consecutive lanes: a
+// partial dot product in-lane (bf16 dot2), the segment sum by xor-shuffles,
+// then a running max over the block's tokens.  Requires H_kv * D to divide
+// 512 (a KiB holds whole tokens).  Only blocks before the local block.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+__device__ __forceinline__ float dot8(bf16x8 x, const bf16x2 (&q)[4]) {
+  float s = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const bf16x2 xp = {x[2 * p], x[2 * p + 1]};
+    s = __builtin_amdgcn_fdot2_f32_bf16(xp, q[p], s, false);
+  }
+  return s;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_scan_kernel(const __bf16* __restrict__ q_idx,
                                                           const __bf16* __restrict__ k_idx,
                                                           int64_t N, int H_kv, int nblk,
                                                           int blocks_per_wave,
                                                           float* __restrict__ P, int64_t ldp) {
+  constexpr int SEG = D / 8;  // lanes per (token, group) segment
   const int b = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tpi = kWave / H_kv;          // tokens per iteration
-  const int tok = lane / H_kv, r = lane % H_kv;
-  float q[D];
-  const __bf16* qp = q_idx + ((int64_t)b * H_kv + r) * D;
+  const int TE = H_kv * D;          // elements per token
+  const int e_lane = 8 * lane;
+  const int r = (e_lane % TE) / D, d0 = e_lane % D;
+  bf16x2 q[4];
+  {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(q_idx + ((int64_t)b * H_kv + r) * D + d0);
 #pragma unroll
-  for (int v = 0; v < D / 8; ++v) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(qp + 8 * v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[8 * v + e] = bf2f(x[e]);
+    for (int p = 0; p < 4; ++p) q[p] = bf16x2{x[2 * p], x[2 * p + 1]};
   }
-  const __bf16* kseq = k_idx + (int64_t)b * N * H_kv * D;
-  const int nb_scan = nblk - 1;  // non-local blocks
+  const __bf16* kseq = k_idx + (int64_t)b * N * TE + e_lane;
+  const int iters = kBlock * TE / 512;  // KiB loads per block (a multiple of 8)
+  const int nb_scan = nblk - 1;        // non-local blocks
   const int blk0 = ((int)blockIdx.x * 4 + wave) * blocks_per_wave;
-  for (int blk = blk0; blk < min(nb_scan, blk0 + blocks_per_wave); ++blk) {
+  const int blk1 = min(nb_scan, blk0 + blocks_per_wave);
+  for (int blk = blk0; blk < blk1; ++blk) {
+    const __bf16* base = kseq + (int64_t)blk * kBlock * TE;
     float m = -INFINITY;
-    for (int t0 = 0; t0 < kBlock; t0 += tpi) {
-      const int64_t j = (int64_t)blk * kBlock + t0 + tok;
-      const __bf16* kr = kseq + (j * H_kv + r) * D;
-      float s = 0.f;
+    for (int u0 = 0; u0 < iters; u0 += 8) {
+      bf16x8 x[8];
 #pragma unroll
-      for (int v = 0; v < D / 8; ++v) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(kr + 8 * v);
+      for (int v = 0; v < 8; ++v)
+        x[v] = *reinterpret_cast<const bf16x8*>(base + (int64_t)512 * (u0 + v));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf(q[8 * v + e], bf2f(x[e]), s);
+      for (int v = 0; v < 8; ++v) {
+        float s = dot8(x[v], q);
+#pragma unroll
+        for (int o = 1; o < SEG; o <<= 1) s += __shfl_xor(s, o, kWave);
+        m = fmaxf(m, s);
       }
-      m = fmaxf(m, s);
     }
-    for (int o = H_kv; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-    if (lane < H_kv) P[((int64_t)b * H_kv + r) * ldp + blk] = m;
+    // lanes at the same offset inside a token hold the same group
+    for (int o = TE / 8; o < kWave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    if (lane < TE / 8 && lane % SEG == 0) P[((int64_t)b * H_kv + r) * ldp + blk] = m;
   }
 }
 
@@ -147,7 +168,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 
 hipError_t launch_decode_scan(const void* q_idx, const void* k_idx, int B, int64_t N, int H_kv,
                               int d_idx, int nblk, float* P, int64_t ldp, hipStream_t stream) {
-  const int bpw = 8;
+  const int bpw = 4;
   const int waves = (int)ceil_div(max(nblk - 1, 1), bpw);
   dim3 grid((unsigned)ceil_div(waves, 4), B), block(256);
   auto* qi = static_cast<const __bf16*>(q_idx);

@@ -103,25 +103,33 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
     if (kb + 1 < kb_end) gload(kb + 1, nxt);
     if (kb < kb_end_w) {
       float m0 = -INFINITY, m1 = -INFINITY;
+      // key-row groups in pairs: the second group's MFMAs overlap the first
+      // group's max-pool
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row = 32 * g + n;
-        bf16x8 a[S];
+      for (int g0 = 0; g0 < 4; g0 += 2) {
+        f32x16 acc[2][2];
 #pragma unroll
-        for (int s = 0; s < S; ++s)
-          a[s] = *reinterpret_cast<const bf16x8*>(
-              &lds[buf][row * D + 8 * (((D / 16) * h + s) ^ kswz<D>(row))]);
-        f32x16 acc0 = {}, acc1 = {};
+        for (int g = 0; g < 2; ++g) {
+          const int row = 32 * (g0 + g) + n;
+          bf16x8 a[S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          acc0 = mfma32(a[s], qb[0][s], acc0);
-          acc1 = mfma32(a[s], qb[1][s], acc1);
+          for (int s = 0; s < S; ++s)
+            a[s] = *reinterpret_cast<const bf16x8*>(
+                &lds[buf][row * D + 8 * (((D / 16) * h + s) ^ kswz<D>(row))]);
+          acc[g][0] = acc[g][1] = f32x16{};
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            acc[g][0] = mfma32(a[s], qb[0][s], acc[g][0]);
+            acc[g][1] = mfma32(a[s], qb[1][s], acc[g][1]);
+          }
         }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          m0 = fmaxf(m0, acc0[j]);
-          m1 = fmaxf(m1, acc1[j]);
-        }
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            m0 = fmaxf(m0, acc[g][0][j]);
+            m1 = fmaxf(m1, acc[g][1][j]);
+          }
       }
       m0 = fmaxf(m0, __shfl_xor(m0, 32, kWave));
       m1 = fmaxf(m1, __shfl_xor(m1, 32, kWave));

@@ -117,9 +117,8 @@ size_t invert_ws(int64_t q_start, int64_t Nq, int H_kv) {
 struct AttnWs {
   int4* items;
   int32_t* n_items;
-  void* Os;
-  float* lse_s;
-  float* Oloc;
+  void* Os;      // bf16 non-local partials [Nq][k-1][d_h/4][H_q][4]
+  float* lse_s;  // their log-sum-exps [Nq][k-1][H_q]
   int64_t max_items;
   size_t bytes;
 };
@@ -133,8 +132,7 @@ AttnWs attn_layout(void* ws, int64_t q_start, int64_t Nq, int H_q, int H_kv, int
   w.items = c.take<int4>(sizeof(int4) * (size_t)w.max_items);
   w.n_items = c.take<int32_t>(sizeof(int32_t));
   w.Os = c.take<void>(2 * (size_t)Nq * (k - 1) * H_q * d_h);
-  w.lse_s = c.take<float>(sizeof(float) * (size_t)Nq * k * H_q);
-  w.Oloc = c.take<float>(sizeof(float) * (size_t)Nq * H_q * d_h);
+  w.lse_s = c.take<float>(sizeof(float) * (size_t)Nq * (k - 1) * H_q);
   w.bytes = c.off;
   return w;
 }
@@ -157,12 +155,12 @@ msa_status run_attn(const void* Q, const void* K, const void* V, const int32_t* 
                              "work-list launch");
   if (st) return st;
   st = hip_status(msa::launch_attn(Q, K, V, col, slot, w.items, w.n_items, w.max_items, q_start,
-                                   Nk, H_q, H_kv, d_h, nblk, k, scale, w.Os, w.lse_s, w.Oloc, s),
+                                   Nk, H_q, H_kv, d_h, nblk, k, scale, w.Os, w.lse_s, s),
                   "attention launch");
   if (st) return st;
-  return hip_status(
-      msa::launch_combine(w.Os, w.lse_s, w.Oloc, q_start, Nq, H_q, d_h, k, O, lse, s),
-      "combine launch");
+  return hip_status(msa::launch_combine(Q, K, V, w.Os, w.lse_s, q_start, Nq, Nk, H_q, H_kv, d_h,
+                                        k, scale, O, lse, s),
+                    "combine launch");
 }
 
 msa_status check_index_dims(int d_idx) {
@@ -357,7 +355,8 @@ msa_status msa_decode(const void* q, const void* q_idx, const void* K, const voi
   if (msa_status st = check_common(0, N, H_kv, B_k, k)) return st;
   if (msa_status st = check_attn_shapes(H_q, H_kv, d_h)) return st;
   if (msa_status st = check_index_dims(d_idx)) return st;
-  if (64 % H_kv) return fail(MSA_ERR_UNSUPPORTED, "decode needs H_kv to divide 64");
+  if (512 % (H_kv * d_idx))
+    return fail(MSA_ERR_UNSUPPORTED, "decode needs H_kv * d_idx to divide 512");
   if (!q || !q_idx || !K || !V || !k_idx || !sel || !O)
     return fail(MSA_ERR_INVALID_ARG, "null q, q_idx, K, V, k_idx, sel or O");
   if (!(scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "scale must be > 0");
@@ -391,7 +390,8 @@ msa_status msa_set_option(int option, int64_t value) {
       g_opt_fused = value;
       return ok();
     case MSA_OPT_ATTN_CHUNK:
-      if (value < 1 || value > (1 << 20)) return fail(MSA_ERR_INVALID_ARG, "chunk out of range");
+      if (value < 1 || value > msa::attn_max_chunk())
+        return fail(MSA_ERR_INVALID_ARG, "chunk must be in [1, %d]", msa::attn_max_chunk());
       g_opt_chunk = value;
       return ok();
     default:

@@ -25,6 +25,7 @@ hipError_t launch_invert(const int32_t* sel, int64_t q_start, int64_t Nq, int H_
                          void* scratch, hipStream_t stream);
 
 // attn.hip
+int attn_max_chunk();
 int64_t attn_max_items(int64_t nb, int64_t nnz, int chunk);
 hipError_t launch_build_items(const int32_t* row_ptr, int64_t nb, int nblk, int64_t q_start,
                               int64_t Nq, int chunk, int4* items, int32_t* n_items,
@@ -33,10 +34,11 @@ hipError_t launch_attn(const void* Q, const void* K, const void* V, const int32_
                        const uint8_t* slot, const int4* items, const int32_t* n_items,
                        int64_t max_items, int64_t q_start, int64_t Nk, int H_q, int H_kv,
                        int d_h, int nblk, int k, float scale, void* Os, float* lse_s,
-                       float* Oloc, hipStream_t stream);
-hipError_t launch_combine(const void* Os, const float* lse_s, const float* Oloc,
-                          int64_t q_start, int64_t Nq, int H_q, int d_h, int k, float* O,
-                          float* lse, hipStream_t stream);
+                       hipStream_t stream);
+hipError_t launch_combine(const void* Q, const void* K, const void* V, const void* Os,
+                          const float* lse_s, int64_t q_start, int64_t Nq, int64_t Nk, int H_q,
+                          int H_kv, int d_h, int k, float scale, float* O, float* lse,
+                          hipStream_t stream);
 
 // decode.hip
 hipError_t launch_decode_scan(const void* q_idx, const void* k_idx, int B, int64_t N, int H_kv,

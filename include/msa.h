@@ -170,7 +170,7 @@ msa_status msa_decode(const void *q, const void *q_idx, const void *K,
  *   MSA_OPT_INDEX_FUSED: 1 = Index Branch as one kernel that keeps a
  *     running Top-k per query next to the score GEMM; 0 = GEMM writes the
  *     block scores, a separate wavefront-per-row Top-k reads them.
- *   MSA_OPT_ATTN_CHUNK: max query positions per KV-outer work item
+ *   MSA_OPT_ATTN_CHUNK: max query positions per KV-outer work item, 1..2048
  *     (section 05 part 2: hot blocks are cut along the query dimension).
  * Returns MSA_ERR_INVALID_ARG for an unknown option or value.
  */

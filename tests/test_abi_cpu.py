@@ -98,7 +98,7 @@ def test_prefill_and_decode_reject(lib):
     assert lib.msa_prefill(*five, 1024, 0, 8, 4, 128, 64, 128, 4, 0.1, NULL, FAKE, NULL,
                            FAKE, 64, NULL) == msa.ERR_WORKSPACE
     assert lib.msa_decode(*five, 2, 1024, 12, 3, 128, 64, 128, 4, 0.1, FAKE, FAKE, NULL,
-                          FAKE, 1 << 30, NULL) == msa.ERR_UNSUPPORTED   # 3 does not divide 64
+                          FAKE, 1 << 30, NULL) == msa.ERR_UNSUPPORTED   # H_kv * d_idx = 192 does not divide 512
     assert lib.msa_decode(*five, 0, 1024, 8, 4, 128, 64, 128, 4, 0.1, FAKE, FAKE, NULL,
                           FAKE, 1 << 30, NULL) == msa.ERR_INVALID_ARG
 
