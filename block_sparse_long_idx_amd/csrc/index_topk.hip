@@ -140,6 +140,30 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
   }
 }
 
+// Work-group -> (group r, query tile).  Work-groups are dispatched to the
+// 8 XCDs round-robin by linear id; when H_kv divides 8, all tiles of a
+// group land on the same 8/H_kv XCDs, so the tiles that sweep that group's
+// key blocks concurrently share them through one L2.  Heaviest tiles (the
+// longest causal rows) first.  Returns false for the padding work-groups.
+__device__ __forceinline__ bool index_tile_of(int w, int ntiles, int H_kv, int& r, int& tile) {
+  int ti;
+  if (8 % H_kv == 0) {
+    const int per = 8 / H_kv;
+    r = (w % 8) / per;
+    ti = (w / 8) * per + (w % per);
+  } else {
+    r = w % H_kv;
+    ti = w / H_kv;
+  }
+  tile = ntiles - 1 - ti;
+  return ti < ntiles;
+}
+
+__host__ __forceinline__ int index_grid(int ntiles, int H_kv) {
+  const int per = (8 % H_kv == 0) ? 8 / H_kv : 1;
+  return (int)ceil_div(ntiles, per) * per * H_kv;
+}
+
 // Sink of the two-kernel variant: stores the pooled scores, 4 blocks at a
 // time, into P[r][q - q_start][kb].
 struct PoolStore {
@@ -160,8 +184,8 @@ __global__ __launch_bounds__(256) void index_pool_kernel(
     int64_t q_start, int64_t Nq, int H_kv, int ntiles, float* __restrict__ P,
     int64_t ldp) {
   __shared__ __attribute__((aligned(16))) __bf16 lds[2][128 * D];
-  const int r = blockIdx.y;
-  const int tile = ntiles - 1 - (int)blockIdx.x;  // long rows first
+  int r, tile;
+  if (!index_tile_of(blockIdx.x, ntiles, H_kv, r, tile)) return;
   const int lane = threadIdx.x & 63;
   const int64_t q_own = q_start + (int64_t)tile * 256 + (threadIdx.x >> 6) * 64 +
                         32 * (lane >> 5) + (lane & 31);
@@ -201,8 +225,8 @@ __global__ __launch_bounds__(256) void index_topk_fused_kernel(
     const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx, int64_t q_start,
     int64_t Nq, int H_kv, int ntiles, int k, int32_t* __restrict__ sel) {
   __shared__ __attribute__((aligned(16))) __bf16 lds[2][128 * D];
-  const int r = blockIdx.y;
-  const int tile = ntiles - 1 - (int)blockIdx.x;  // long rows first
+  int r, tile;
+  if (!index_tile_of(blockIdx.x, ntiles, H_kv, r, tile)) return;
   const int lane = threadIdx.x & 63;
   const int64_t q_own = q_start + (int64_t)tile * 256 + (threadIdx.x >> 6) * 64 +
                         32 * (lane >> 5) + (lane & 31);
@@ -239,7 +263,7 @@ hipError_t launch_index_pool(const void* q_idx, const void* k_idx, int64_t q_sta
                              int64_t Nq, int H_kv, int d_idx, float* P, int64_t ldp,
                              hipStream_t stream) {
   const int ntiles = (int)ceil_div(Nq, 256);
-  dim3 grid(ntiles, H_kv), block(256);
+  dim3 grid(index_grid(ntiles, H_kv)), block(256);
   auto* qi = static_cast<const __bf16*>(q_idx);
   auto* ki = static_cast<const __bf16*>(k_idx);
   switch (d_idx) {
@@ -364,7 +388,7 @@ template <int D>
 static void launch_fused_d(const __bf16* qi, const __bf16* ki, int64_t q_start, int64_t Nq,
                            int H_kv, int k, int32_t* sel, hipStream_t stream) {
   const int ntiles = (int)ceil_div(Nq, 256);
-  dim3 grid(ntiles, H_kv), block(256);
+  dim3 grid(index_grid(ntiles, H_kv)), block(256);
   if (k <= 8)
     index_topk_fused_kernel<D, 7><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
   else if (k <= 16)
