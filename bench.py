@@ -37,6 +37,32 @@ def formula_flops(cfg):
     return main, index
 
 
+def stored_traffic(kernel):
+    """HBM bytes per launch of `kernel` measured with rocprofv3 FETCH_SIZE /
+    WRITE_SIZE (calibrated on a plain copy), from profiles/; None once the
+    kernel's sources differ from the ones that were profiled."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "prefill_1m_hbm_traffic.md")
+    srcs = [os.path.join(ROOT, "block_sparse_long_idx_amd", "csrc", f)
+            for f in ("index_topk.hip", "common.h")]
+    try:
+        h = hashlib.sha256()
+        for f in srcs:
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+        with open(path) as fh:
+            for line in fh:
+                parts = line.split()
+                if len(parts) == 5 and parts[0] == "traffic" and parts[1] == kernel:
+                    kv = dict(x.split("=") for x in parts[2:])
+                    if kv["sources"] != h.hexdigest()[:16]:
+                        return None
+                    return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+    except OSError:
+        return None
+    return None
+
+
 def chunks_of(cfg):
     c = cfg.chunk or cfg.N
     return [(q0, min(c, cfg.N - q0)) for q0 in range(0, cfg.N, c)]
@@ -194,6 +220,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K and decode legs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -201,6 +229,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        # A plain copy of known size: reads and writes exactly 1 GiB each, so
+        # FETCH_SIZE / WRITE_SIZE of this dispatch calibrate the counters.
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4}))
+        return
     from block_sparse_long_idx_amd import msa
     from block_sparse_long_idx_amd.synth import CONFIGS, inputs_for
     msa.load()
@@ -225,9 +263,11 @@ def main():
         ach = index_f / (stages[0] / 1e3) / 1e12
         roof = {"kernel": "index_topk_fused_kernel", "bound": "mfma",
                 "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic("index_topk_fused_kernel") if cfg.name == "1m" else None,
                 "per_launch": f"{len(pf.chunks)} launches per step, one per query chunk; "
-                              "algorithmic flops = H_kv*d_idx*N^2 per step"}
+                              "achieved = algorithmic flops (H_kv*d_idx*N^2 per step) / "
+                              "the launches' event time; traffic in HBM bytes per launch"}
     else:
         roof = {"kernel": stage_names[dom], "bound": "hbm", "achieved": None,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": None, "traffic": None}
