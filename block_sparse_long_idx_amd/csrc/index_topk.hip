@@ -32,9 +32,10 @@ namespace msa {
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ int kswz(int row) {
-  // XOR swizzle of the 16-byte chunk index inside a key row so that 8
-  // consecutive rows read at the same logical chunk hit distinct banks.
-  return D == 32 ? ((row >> 1) & 3) : (row & 7);
+  // XOR swizzle of the 16-byte chunk index inside a key row: the 16 rows that
+  // one 128-bit LDS read cycle serves (16 lanes x 16 B = 256 B) then hit 16
+  // distinct 16-byte bank groups.
+  return D == 32 ? ((row >> 2) & 3) : D == 64 ? ((row >> 1) & 7) : (row & 15);
 }
 
 // The sweep shared by both Index-Branch variants.  For every key block kb
@@ -98,6 +99,10 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
   }
   __syncthreads();
 
+  // The sink takes block kb-1's pooled score while block kb's MFMAs are in
+  // flight, so its VALU work can issue under them.
+  int kb_prev = -1;
+  float v_prev = -INFINITY;
   for (int kb = 0; kb < kb_end; ++kb) {
     const int buf = kb & 1;
     if (kb + 1 < kb_end) gload(kb + 1, nxt);
@@ -123,6 +128,7 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
             acc[g][1] = mfma32(a[s], qb[1][s], acc[g][1]);
           }
         }
+        if (g0 == 0 && kb_prev >= 0) sink(kb_prev, kb_end_w, v_prev);
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -133,11 +139,13 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
       }
       m0 = fmaxf(m0, __shfl_xor(m0, 32, kWave));
       m1 = fmaxf(m1, __shfl_xor(m1, 32, kWave));
-      sink(kb, kb_end_w, h ? m1 : m0);
+      kb_prev = kb;
+      v_prev = h ? m1 : m0;
     }
     if (kb + 1 < kb_end) lstore(buf ^ 1, nxt);
     __syncthreads();
   }
+  if (kb_prev >= 0) sink(kb_prev, kb_end_w, v_prev);
 }
 
 // Work-group -> (group r, query tile).  Work-groups are dispatched to the
@@ -204,7 +212,9 @@ struct TopkKeep {
   float sc[LM];
   int bk[LM];
   __device__ __forceinline__ void operator()(int kb, int, float v) {
-    if (kb < lb_own && v > sc[LM - 1]) {
+    // A block that must not enter (the local block or later) becomes -inf.
+    v = kb < lb_own ? v : -INFINITY;
+    if (v > sc[LM - 1]) {
 #pragma unroll
       for (int j = LM - 1; j > 0; --j) {
         const bool up = v > sc[j - 1];
@@ -212,10 +222,8 @@ struct TopkKeep {
         sc[j] = up ? sc[j - 1] : (here ? v : sc[j]);
         bk[j] = up ? bk[j - 1] : (here ? kb : bk[j]);
       }
-      if (v > sc[0]) {
-        sc[0] = v;
-        bk[0] = kb;
-      }
+      bk[0] = v > sc[0] ? kb : bk[0];
+      sc[0] = v > sc[0] ? v : sc[0];
     }
   }
 };
