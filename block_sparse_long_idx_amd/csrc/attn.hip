@@ -17,14 +17,17 @@
 // their local block, in fp32 all the way.
 //
 // Partial precision: O_s in bf16 (the pages' IO accounting is bf16), lse_s
-// in fp32.  Workspace layouts (d_h = DH):
-//   Os    bf16 [Nq][k-1][DH/4][H_q][4]   non-local slot s of position iq
+// in fp32.  Workspace layouts (d_h = DH, G heads per group):
+//   Os    bf16 [Nq][k-1][H_kv][DH/4][G][4]   non-local slot s of position iq
 //   lse_s fp32 [Nq][k-1][H_q]
-// Four consecutive d of consecutive heads are adjacent, so the 16 heads of
-// a position that one MFMA tile holds store 128 contiguous bytes per
-// instruction, and the combine reads them back the same way.
+// One (position, slot, group) partial is G * DH contiguous values, and
+// within it four consecutive d of consecutive heads are adjacent, so the G
+// heads of a position that one MFMA tile holds store G * 8 contiguous
+// bytes per instruction, and the combine reads them back the same way.
 #include "common.h"
 #include "msa_internal.h"
+
+#include <algorithm>
 
 namespace msa {
 
@@ -47,38 +50,51 @@ __device__ __forceinline__ void bucket_items(int64_t bucket, const int32_t* row_
   items = (n_non + chunk - 1) / chunk;
 }
 
+// Items go out heaviest first -- every full item (exactly `chunk` positions)
+// in bucket order, then the buckets' remainders -- so the work-groups that
+// fetch items last get short ones.  n_items[0] = item count; n_items[1] is
+// the attention kernel's fetch counter, cleared here.
 __global__ __launch_bounds__(1024) void build_items_kernel(const int32_t* __restrict__ row_ptr,
                                                            int64_t nb, int nblk, int64_t q_start,
                                                            int64_t Nq, int chunk,
                                                            int4* __restrict__ items,
                                                            int32_t* __restrict__ n_items) {
-  __shared__ int32_t part[1024];
+  __shared__ int32_t full[1024], rest[1024];
   const int t = threadIdx.x;
   const int64_t per = ceil_div(nb, 1024);
   const int64_t lo = min(nb, per * t), hi = min(nb, per * (t + 1));
-  int32_t s = 0;
+  int32_t nf = 0, nr = 0;
   for (int64_t x = lo; x < hi; ++x) {
-    int32_t a, c, it;
-    bucket_items(x, row_ptr, nblk, q_start, Nq, chunk, a, c, it);
-    s += it;
+    int32_t n_loc, n_non, it;
+    bucket_items(x, row_ptr, nblk, q_start, Nq, chunk, n_loc, n_non, it);
+    nf += n_non / chunk;
+    nr += n_non % chunk != 0;
   }
-  part[t] = s;
+  full[t] = nf;
+  rest[t] = nr;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
-    const int32_t v = t >= o ? part[t - o] : 0;
+    const int32_t vf = t >= o ? full[t - o] : 0, vr = t >= o ? rest[t - o] : 0;
     __syncthreads();
-    part[t] += v;
+    full[t] += vf;
+    rest[t] += vr;
     __syncthreads();
   }
-  int32_t pos = t ? part[t - 1] : 0;
+  const int32_t n_full = full[1023];
+  int32_t pf = t ? full[t - 1] : 0, pr = n_full + (t ? rest[t - 1] : 0);
   for (int64_t x = lo; x < hi; ++x) {
     int32_t n_loc, n_non, it;
     bucket_items(x, row_ptr, nblk, q_start, Nq, chunk, n_loc, n_non, it);
     const int32_t start = row_ptr[x] + n_loc;
-    for (int32_t done = 0; done < n_non; done += chunk)
-      items[pos++] = make_int4((int)x, start + done, min(chunk, n_non - done), 0);
+    int32_t done = 0;
+    for (; done + chunk <= n_non; done += chunk)
+      items[pf++] = make_int4((int)x, start + done, chunk, 0);
+    if (done < n_non) items[pr++] = make_int4((int)x, start + done, n_non - done, 0);
   }
-  if (t == 1023) *n_items = part[1023];
+  if (t == 1023) {
+    n_items[0] = n_full + rest[1023];
+    n_items[1] = 0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -110,6 +126,17 @@ struct AttnSmem {
 
 __device__ __forceinline__ int vt_off(int d, int key) { return d * kVtPitch + key; }
 
+// XOR swizzle of the 16-byte chunks of K row `row` in LDS.  A fragment read
+// has 16 lanes (16 consecutive rows, one chunk index) in flight per LDS
+// cycle; the swizzle sends them to 16 distinct 4-bank groups.  d_h = 128:
+// a row spans all 64 banks, so rows differ in their low 4 bits.  d_h = 64:
+// two rows share a bank row (row & 1 picks the half), so the next 3 bits
+// pick the chunk.
+template <int DH>
+__device__ __forceinline__ int k_swz(int row) {
+  return DH == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
 // K and V of block (group r, keys key0..key0+127); keys >= Nk read as 0.
 template <int DH>
 __device__ __forceinline__ void stage_kv(AttnSmem<DH>& sm, const __bf16* __restrict__ K,
@@ -121,7 +148,7 @@ __device__ __forceinline__ void stage_kv(AttnSmem<DH>& sm, const __bf16* __restr
     bf16x8 v = {};
     if (key0 + row < Nk)
       v = *reinterpret_cast<const bf16x8*>(K + ((key0 + row) * H_kv + r) * DH + 8 * c);
-    *reinterpret_cast<bf16x8*>(&sm.k[row * DH + 8 * (c ^ (row & 7))]) = v;
+    *reinterpret_cast<bf16x8*>(&sm.k[row * DH + 8 * (c ^ k_swz<DH>(row))]) = v;
   }
   for (int id = t; id < (kBlock / 4) * CH; id += 256) {
     const int kq = id % (kBlock / 4), c = id / (kBlock / 4);  // 4 keys x 8 d
@@ -179,7 +206,7 @@ template <int DH>
 __device__ __forceinline__ bf16x8 k_frag(const AttnSmem<DH>& sm, int g, int s, int h, int n) {
   const int krow = 32 * g + n;
   return *reinterpret_cast<const bf16x8*>(
-      &sm.k[krow * DH + 8 * (((DH / 16) * h + s) ^ (krow & 7))]);
+      &sm.k[krow * DH + 8 * (((DH / 16) * h + s) ^ k_swz<DH>(krow))]);
 }
 
 // V^T fragment (MFMA A: 32 d x 16 keys) for d = 32*dg + n and the keys of
@@ -204,8 +231,8 @@ __device__ __forceinline__ bf16x8 v_frag(const AttnSmem<DH>& sm, int dg, int g, 
 // ---------------------------------------------------------------------------
 template <int DH>
 __device__ __forceinline__ void attn_item(const AttnSmem<DH>& sm, const __bf16* __restrict__ Q,
-                                          int nrows, int wave, int r, int G, int H_q, int k,
-                                          int64_t q_start, float scale_log2,
+                                          int nrows, int wave, int r, int G, int H_q, int H_kv,
+                                          int k, int64_t q_start, float scale_log2,
                                           __bf16* __restrict__ Os, float* __restrict__ lse_s,
                                           int h, int n) {
   constexpr int S = DH / 16;
@@ -295,13 +322,13 @@ __device__ __forceinline__ void attn_item(const AttnSmem<DH>& sm, const __bf16* 
         const float inv = 1.f / l[c];
         const int iq = row[c].pos - (int)q_start;
         // d = 32dg + 8qd + 4h + e  ->  group of four dq = 8dg + 2qd + h
-        __bf16* dst = Os + (int64_t)(iq * (k - 1) + row[c].sl) * (DH / 4) * H_q * 4 +
-                      row[c].hq * 4;
+        __bf16* dst = Os + ((int64_t)(iq * (k - 1) + row[c].sl) * H_kv + r) * (DH / 4) * G * 4 +
+                      (row[c].hq - r * G) * 4;
 #pragma unroll
         for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd)
-            *reinterpret_cast<bf16x4*>(dst + (8 * (2 * half + dd) + 2 * qd + h) * H_q * 4) =
+            *reinterpret_cast<bf16x4*>(dst + (8 * (2 * half + dd) + 2 * qd + h) * G * 4) =
                 bf16x4{f2bf(oacc[c][dd][4 * qd] * inv), f2bf(oacc[c][dd][4 * qd + 1] * inv),
                        f2bf(oacc[c][dd][4 * qd + 2] * inv), f2bf(oacc[c][dd][4 * qd + 3] * inv)};
       }
@@ -321,25 +348,34 @@ template <int DH>
 __global__ __launch_bounds__(256, 2) void attn_kv_outer_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ col, const uint8_t* __restrict__ slot,
-    const int4* __restrict__ items, const int32_t* __restrict__ n_items, int64_t q_start,
+    const int4* __restrict__ items, int32_t* __restrict__ n_items, int64_t q_start,
     int64_t Nk, int H_q, int H_kv, int G, int nblk, int k, float scale_log2,
     __bf16* __restrict__ Os, float* __restrict__ lse_s) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   AttnSmem<DH>& sm = *reinterpret_cast<AttnSmem<DH>*>(smem_raw);
-  const int item_id = blockIdx.x;
-  if (item_id >= *n_items) return;
-  const int4 it = items[item_id];
-  const int bucket = it.x, start = it.y, count = it.z;
-  const int r = bucket / nblk, b = bucket % nblk;
+  __shared__ int32_t next;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  for (int p = t; p < count; p += 256) {
-    sm.pos[p] = col[start + p];
-    sm.sl[p] = slot[start + p];
+  const int32_t total = n_items[0];
+  // Persistent work-groups fetch items in list order until the list is
+  // exhausted; every wave of a work-group sees the same fetched index.
+  for (;;) {
+    if (t == 0) next = atomicAdd(&n_items[1], 1);
+    __syncthreads();
+    const int32_t item_id = next;
+    if (item_id >= total) return;
+    const int4 it = items[item_id];
+    const int bucket = it.x, start = it.y, count = it.z;
+    const int r = bucket / nblk, b = bucket % nblk;
+    for (int p = t; p < count; p += 256) {
+      sm.pos[p] = col[start + p];
+      sm.sl[p] = slot[start + p];
+    }
+    stage_kv<DH>(sm, K, V, r, H_kv, (int64_t)b * kBlock, Nk, t);
+    __syncthreads();
+    attn_item<DH>(sm, Q, count * G, wave, r, G, H_q, H_kv, k, q_start, scale_log2, Os, lse_s,
+                  lane >> 5, lane & 31);
+    __syncthreads();  // LDS and `next` are reused by the next item
   }
-  stage_kv<DH>(sm, K, V, r, H_kv, (int64_t)b * kBlock, Nk, t);
-  __syncthreads();
-  attn_item<DH>(sm, Q, count * G, wave, r, G, H_q, k, q_start, scale_log2, Os, lse_s,
-                lane >> 5, lane & 31);
 }
 
 // ---------------------------------------------------------------------------
@@ -452,7 +488,8 @@ __global__ __launch_bounds__(256, 2) void combine_local_kernel(
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[dg][j] = 0.f;
     float den = 0.f;
-    const __bf16* src = Os + (int64_t)iq * (k - 1) * (DH / 4) * H_q * 4 + row.hq * 4;
+    const __bf16* src =
+        Os + ((int64_t)iq * (k - 1) * H_kv + r) * (DH / 4) * G * 4 + (row.hq - r * G) * 4;
     for (int s = 0; s < n_sel - 1; ++s) {
       const float w = __expf(ls[s * H_q] - M);
       den += w;
@@ -462,7 +499,7 @@ __global__ __launch_bounds__(256, 2) void combine_local_kernel(
       for (int dg = 0; dg < NDG; ++dg)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
-          x[dg][qd] = *reinterpret_cast<const bf16x4*>(ps + (8 * dg + 2 * qd + h) * H_q * 4);
+          x[dg][qd] = *reinterpret_cast<const bf16x4*>(ps + (8 * dg + 2 * qd + h) * G * 4);
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg)
 #pragma unroll
@@ -520,8 +557,23 @@ static hipError_t attn_prepare() {
   return e;
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 hipError_t launch_attn(const void* Q, const void* K, const void* V, const int32_t* col,
-                       const uint8_t* slot, const int4* items, const int32_t* n_items,
+                       const uint8_t* slot, const int4* items, int32_t* n_items,
                        int64_t max_items, int64_t q_start, int64_t Nk, int H_q, int H_kv,
                        int d_h, int nblk, int k, float scale, void* Os, float* lse_s,
                        hipStream_t stream) {
@@ -534,7 +586,8 @@ hipError_t launch_attn(const void* Q, const void* K, const void* V, const int32_
   auto* kk = static_cast<const __bf16*>(K);
   auto* v = static_cast<const __bf16*>(V);
   auto* os = static_cast<__bf16*>(Os);
-  dim3 grid((unsigned)max_items), block(256);
+  // Two resident work-groups per CU (the kernel's occupancy).
+  dim3 grid((unsigned)std::min<int64_t>(max_items, 2 * (int64_t)device_cus())), block(256);
   if (d_h == 128)
     attn_kv_outer_kernel<128><<<grid, block, sizeof(AttnSmem<128>), stream>>>(
         q, kk, v, col, slot, items, n_items, q_start, Nk, H_q, H_kv, G, nblk, k, scale_log2, os,

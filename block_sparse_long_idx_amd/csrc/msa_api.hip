@@ -130,7 +130,7 @@ AttnWs attn_layout(void* ws, int64_t q_start, int64_t Nq, int H_q, int H_kv, int
   Carve c(ws);
   w.max_items = msa::attn_max_items((int64_t)H_kv * nblk, nnz, (int)g_opt_chunk);
   w.items = c.take<int4>(sizeof(int4) * (size_t)w.max_items);
-  w.n_items = c.take<int32_t>(sizeof(int32_t));
+  w.n_items = c.take<int32_t>(2 * sizeof(int32_t));  // count, fetch counter
   w.Os = c.take<void>(2 * (size_t)Nq * (k - 1) * H_q * d_h);
   w.lse_s = c.take<float>(sizeof(float) * (size_t)Nq * (k - 1) * H_q);
   w.bytes = c.off;
