@@ -20,6 +20,8 @@
 // in fp32.  Workspace layouts (d_h = DH, G heads per group):
 //   Os    bf16 [Nq][k-1][H_kv][DH/4][G][4]   non-local slot s of position iq
 //   lse_s fp32 [Nq][k-1][H_q]
+// plus one spare slot after the last, written (never read) by MFMA rows
+// past the end of a work item.
 // One (position, slot, group) partial is G * DH contiguous values, and
 // within it four consecutive d of consecutive heads are adjacent, so the G
 // heads of a position that one MFMA tile holds store G * 8 contiguous
@@ -168,7 +170,12 @@ __device__ __forceinline__ void stage_kv(AttnSmem<DH>& sm, const __bf16* __restr
 }
 
 // Row of a 32-row tile held by this lane: item row R = tile*32 + n is
-// (position R / G of the item, head R % G of the group).
+// (position R / G of the item, head R % G of the group).  R / G is taken as
+// trunc((R + 1/2) * inv_G) in fp32 with inv_G = fp32(1 / G): the true
+// quotient plus 1/(2G) stays at least 1/(2G) >= 1/128 away from the next
+// integer, far beyond the rounding error for R < 2^17 and G <= 64 (rows per
+// item <= 2048 * 64); it keeps the integer division and its spilled
+// reciprocal out of the tile loop.
 struct TileRow {
   int pos;  // absolute query position (< 2^31)
   int hq, sl;
@@ -177,14 +184,14 @@ struct TileRow {
 
 template <int DH>
 __device__ __forceinline__ TileRow tile_row(const AttnSmem<DH>& sm, int nrows, int tile, int r,
-                                            int G, int n) {
+                                            int G, float inv_G, int n) {
   TileRow t{0, 0, 0, false};
   const int R = tile * 32 + n;
   if (R < nrows) {
-    const int p = R / G;
+    const int p = (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G);
     t.pos = sm.pos[p];
     t.sl = sm.sl[p];
-    t.hq = r * G + R % G;
+    t.hq = r * G + (R - p * G);
     t.ok = true;
   }
   return t;
@@ -226,13 +233,41 @@ __device__ __forceinline__ bf16x8 v_frag(const AttnSmem<DH>& sm, int dg, int g, 
 // wave, as two 32-row halves c = 0, 1 that share every K and V^T fragment
 // read from LDS (each fragment feeds two MFMAs).  P is kept in bf16
 // registers and O is produced in halves of d so the accumulators fit two
-// waves per SIMD.  The next tile's Q rows are fetched into the Q registers
-// once the softmax is done, overlapping the gather with PV and the stores.
+// waves per SIMD.
+//
+// Memory pipeline: the next tile's Q rows are fetched into the Q registers
+// once the softmax is done, then this tile's partials are stored; the loop
+// is rotated so that the next tile's S^T follows the stores in straight-
+// line code, and every store is unconditional (rows past the item's end
+// write to the spare slot `spare` instead), so the wait for the Q rows
+// leaves the stores in flight.
 // ---------------------------------------------------------------------------
 template <int DH>
+__device__ __forceinline__ void s_tile(const AttnSmem<DH>& sm, const bf16x8 (&qb)[2][DH / 16],
+                                       f32x16 (&sacc)[2][4], int h, int n) {
+  constexpr int S = DH / 16;
+#pragma unroll
+  for (int g0 = 0; g0 < 4; g0 += 2) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) sacc[c][g0] = sacc[c][g0 + 1] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+#pragma unroll
+      for (int g = g0; g < g0 + 2; ++g) {
+        const bf16x8 a = k_frag<DH>(sm, g, s, h, n);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) sacc[c][g] = mfma32(a, qb[c][s], sacc[c][g]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int DH>
 __device__ __forceinline__ void attn_item(const AttnSmem<DH>& sm, const __bf16* __restrict__ Q,
-                                          int nrows, int wave, int r, int G, int H_q, int H_kv,
-                                          int k, int64_t q_start, float scale_log2,
+                                          int nrows, int wave, int r, int G, float inv_G,
+                                          int H_q, int H_kv, int k, int64_t q_start,
+                                          int64_t spare, float scale_log2,
                                           __bf16* __restrict__ Os, float* __restrict__ lse_s,
                                           int h, int n) {
   constexpr int S = DH / 16;
@@ -243,27 +278,12 @@ __device__ __forceinline__ void attn_item(const AttnSmem<DH>& sm, const __bf16* 
   bf16x8 qb[2][S];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    row[c] = tile_row<DH>(sm, nrows, 2 * wave + c, r, G, n);
+    row[c] = tile_row<DH>(sm, nrows, 2 * wave + c, r, G, inv_G, n);
     load_q<DH>(qb[c], Q, row[c], H_q, h);
   }
-  for (int tile = wave; tile < ntile; tile += 4) {
-    // ---- S^T = K . Q^T for both halves ----------------------------------------
-    f32x16 sacc[2][4];
-#pragma unroll
-    for (int g0 = 0; g0 < 4; g0 += 2) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) sacc[c][g0] = sacc[c][g0 + 1] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-#pragma unroll
-        for (int g = g0; g < g0 + 2; ++g) {
-          const bf16x8 a = k_frag<DH>(sm, g, s, h, n);
-#pragma unroll
-          for (int c = 0; c < 2; ++c) sacc[c][g] = mfma32(a, qb[c][s], sacc[c][g]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  f32x16 sacc[2][4];
+  s_tile<DH>(sm, qb, sacc, h, n);
+  for (int tile = wave;;) {
     // ---- softmax: P in bf16, row sums l ---------------------------------------
     bf16x8 pb[2][4][2];
     float mb[2], l[2];
@@ -290,14 +310,24 @@ __device__ __forceinline__ void attn_item(const AttnSmem<DH>& sm, const __bf16* 
       l[c] = ls + __shfl_xor(ls, 32, kWave);
     }
     // ---- prefetch the next tile's Q into qb -----------------------------------
+    const bool more = tile + 4 < ntile;
     TileRow nrow[2] = {{0, 0, 0, false}, {0, 0, 0, false}};
-    if (tile + 4 < ntile) {
+    if (more) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) nrow[c] = tile_row<DH>(sm, nrows, 2 * (tile + 4) + c, r, G, n);
+      for (int c = 0; c < 2; ++c)
+        nrow[c] = tile_row<DH>(sm, nrows, 2 * (tile + 4) + c, r, G, inv_G, n);
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) load_q<DH>(qb[c], Q, nrow[c], H_q, h);
     // ---- O^T = V^T . P^T in halves of d, stored as bf16 partials -------------
+    // Partial (iq, slot) of the row, or the spare slot for rows past the end.
+    int64_t ps[2];
+    float inv[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      ps[c] = row[c].ok ? (int64_t)(row[c].pos - (int)q_start) * (k - 1) + row[c].sl : spare;
+      inv[c] = 1.f / l[c];
+    }
 #pragma unroll
     for (int half = 0; half < NDG / 2; ++half) {
       f32x16 oacc[2][2];
@@ -318,29 +348,31 @@ __device__ __forceinline__ void attn_item(const AttnSmem<DH>& sm, const __bf16* 
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        if (!row[c].ok) continue;
-        const float inv = 1.f / l[c];
-        const int iq = row[c].pos - (int)q_start;
-        // d = 32dg + 8qd + 4h + e  ->  group of four dq = 8dg + 2qd + h
-        __bf16* dst = Os + ((int64_t)(iq * (k - 1) + row[c].sl) * H_kv + r) * (DH / 4) * G * 4 +
-                      (row[c].hq - r * G) * 4;
+        // d = 32dg + 8qd + 4h + e  ->  d-quad 8dg + 2qd + h; the lane's h and
+        // head go into the pointer, the rest is a wave-uniform offset.
+        __bf16* dst = Os + (ps[c] * H_kv + r) * (DH / 4) * G * 4 +
+                      (row[c].hq - r * G + h * G) * 4;
 #pragma unroll
         for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd)
-            *reinterpret_cast<bf16x4*>(dst + (8 * (2 * half + dd) + 2 * qd + h) * G * 4) =
-                bf16x4{f2bf(oacc[c][dd][4 * qd] * inv), f2bf(oacc[c][dd][4 * qd + 1] * inv),
-                       f2bf(oacc[c][dd][4 * qd + 2] * inv), f2bf(oacc[c][dd][4 * qd + 3] * inv)};
+            *reinterpret_cast<bf16x4*>(dst + (8 * (2 * half + dd) + 2 * qd) * G * 4) =
+                bf16x4{f2bf(oacc[c][dd][4 * qd] * inv[c]),
+                       f2bf(oacc[c][dd][4 * qd + 1] * inv[c]),
+                       f2bf(oacc[c][dd][4 * qd + 2] * inv[c]),
+                       f2bf(oacc[c][dd][4 * qd + 3] * inv[c])};
       }
       __builtin_amdgcn_sched_barrier(0);  // one half's accumulators live at a time
     }
+    // Both lane halves hold the row's lse; both store it (same value).
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      if (row[c].ok && h == 0)
-        lse_s[(int64_t)((row[c].pos - (int)q_start) * (k - 1) + row[c].sl) * H_q + row[c].hq] =
-            (mb[c] + log2f(l[c])) * 0.69314718055994531f;
+      lse_s[ps[c] * H_q + row[c].hq] = (mb[c] + log2f(l[c])) * 0.69314718055994531f;
+    if (!more) break;
+    tile += 4;
 #pragma unroll
     for (int c = 0; c < 2; ++c) row[c] = nrow[c];
+    s_tile<DH>(sm, qb, sacc, h, n);
   }
 }
 
@@ -349,8 +381,8 @@ __global__ __launch_bounds__(256, 2) void attn_kv_outer_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ col, const uint8_t* __restrict__ slot,
     const int4* __restrict__ items, int32_t* __restrict__ n_items, int64_t q_start,
-    int64_t Nk, int H_q, int H_kv, int G, int nblk, int k, float scale_log2,
-    __bf16* __restrict__ Os, float* __restrict__ lse_s) {
+    int64_t Nk, int H_q, int H_kv, int G, float inv_G, int nblk, int k, int64_t spare,
+    float scale_log2, __bf16* __restrict__ Os, float* __restrict__ lse_s) {
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   AttnSmem<DH>& sm = *reinterpret_cast<AttnSmem<DH>*>(smem_raw);
   __shared__ int32_t next;
@@ -372,8 +404,8 @@ __global__ __launch_bounds__(256, 2) void attn_kv_outer_kernel(
     }
     stage_kv<DH>(sm, K, V, r, H_kv, (int64_t)b * kBlock, Nk, t);
     __syncthreads();
-    attn_item<DH>(sm, Q, count * G, wave, r, G, H_q, H_kv, k, q_start, scale_log2, Os, lse_s,
-                  lane >> 5, lane & 31);
+    attn_item<DH>(sm, Q, count * G, wave, r, G, inv_G, H_q, H_kv, k, q_start, spare,
+                  scale_log2, Os, lse_s, lane >> 5, lane & 31);
     __syncthreads();  // LDS and `next` are reused by the next item
   }
 }
@@ -391,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void attn_kv_outer_kernel(
 template <int DH>
 __global__ __launch_bounds__(256, 2) void combine_local_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    int64_t q_start, int64_t Nq, int64_t Nk, int H_q, int H_kv, int G, int k,
+    int64_t q_start, int64_t Nq, int64_t Nk, int H_q, int H_kv, int G, float inv_G, int k,
     float scale_log2, const __bf16* __restrict__ Os, const float* __restrict__ lse_s,
     float* __restrict__ O, float* __restrict__ lse) {
   constexpr int S = DH / 16;
@@ -416,7 +448,7 @@ __global__ __launch_bounds__(256, 2) void combine_local_kernel(
   const int nrows = npos * G;
   const int ntile = (nrows + 31) / 32;
   for (int tile = wave; tile < ntile; tile += 4) {
-    const TileRow row = tile_row<DH>(sm, nrows, tile, r, G, n);
+    const TileRow row = tile_row<DH>(sm, nrows, tile, r, G, inv_G, n);
     // ---- local block: S^T with the causal mask --------------------------------
     f32x16 sacc[4];
     {
@@ -574,13 +606,15 @@ static int device_cus() {
 
 hipError_t launch_attn(const void* Q, const void* K, const void* V, const int32_t* col,
                        const uint8_t* slot, const int4* items, int32_t* n_items,
-                       int64_t max_items, int64_t q_start, int64_t Nk, int H_q, int H_kv,
-                       int d_h, int nblk, int k, float scale, void* Os, float* lse_s,
+                       int64_t max_items, int64_t q_start, int64_t Nq, int64_t Nk, int H_q,
+                       int H_kv, int d_h, int nblk, int k, float scale, void* Os, float* lse_s,
                        hipStream_t stream) {
   hipError_t e = attn_prepare();
   if (e != hipSuccess) return e;
   if (k < 2) return hipSuccess;  // no non-local blocks
   const int G = H_q / H_kv;
+  const int64_t spare = Nq * (k - 1);  // the slot after the last real one
+  const float inv_G = 1.f / (float)G;
   const float scale_log2 = scale * 1.4426950408889634f;
   auto* q = static_cast<const __bf16*>(Q);
   auto* kk = static_cast<const __bf16*>(K);
@@ -590,12 +624,12 @@ hipError_t launch_attn(const void* Q, const void* K, const void* V, const int32_
   dim3 grid((unsigned)std::min<int64_t>(max_items, 2 * (int64_t)device_cus())), block(256);
   if (d_h == 128)
     attn_kv_outer_kernel<128><<<grid, block, sizeof(AttnSmem<128>), stream>>>(
-        q, kk, v, col, slot, items, n_items, q_start, Nk, H_q, H_kv, G, nblk, k, scale_log2, os,
-        lse_s);
+        q, kk, v, col, slot, items, n_items, q_start, Nk, H_q, H_kv, G, inv_G, nblk, k, spare,
+        scale_log2, os, lse_s);
   else if (d_h == 64)
     attn_kv_outer_kernel<64><<<grid, block, sizeof(AttnSmem<64>), stream>>>(
-        q, kk, v, col, slot, items, n_items, q_start, Nk, H_q, H_kv, G, nblk, k, scale_log2, os,
-        lse_s);
+        q, kk, v, col, slot, items, n_items, q_start, Nk, H_q, H_kv, G, inv_G, nblk, k, spare,
+        scale_log2, os, lse_s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -608,6 +642,7 @@ hipError_t launch_combine(const void* Q, const void* K, const void* V, const voi
   hipError_t e = attn_prepare();
   if (e != hipSuccess) return e;
   const int G = H_q / H_kv;
+  const float inv_G = 1.f / (float)G;
   const float scale_log2 = scale * 1.4426950408889634f;
   const int64_t nqb = (q_start + Nq - 1) / kBlock - q_start / kBlock + 1;
   dim3 grid((unsigned)nqb, H_kv), block(256);
@@ -617,10 +652,10 @@ hipError_t launch_combine(const void* Q, const void* K, const void* V, const voi
   auto* os = static_cast<const __bf16*>(Os);
   if (d_h == 128)
     combine_local_kernel<128><<<grid, block, sizeof(AttnSmem<128>), stream>>>(
-        q, kk, v, q_start, Nq, Nk, H_q, H_kv, G, k, scale_log2, os, lse_s, O, lse);
+        q, kk, v, q_start, Nq, Nk, H_q, H_kv, G, inv_G, k, scale_log2, os, lse_s, O, lse);
   else if (d_h == 64)
     combine_local_kernel<64><<<grid, block, sizeof(AttnSmem<64>), stream>>>(
-        q, kk, v, q_start, Nq, Nk, H_q, H_kv, G, k, scale_log2, os, lse_s, O, lse);
+        q, kk, v, q_start, Nq, Nk, H_q, H_kv, G, inv_G, k, scale_log2, os, lse_s, O, lse);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -117,8 +117,8 @@ size_t invert_ws(int64_t q_start, int64_t Nq, int H_kv) {
 struct AttnWs {
   int4* items;
   int32_t* n_items;
-  void* Os;      // bf16 non-local partials [Nq][k-1][d_h/4][H_q][4]
-  float* lse_s;  // their log-sum-exps [Nq][k-1][H_q]
+  void* Os;      // bf16 non-local partials [Nq*(k-1) + 1][H_kv][d_h/4][G][4]
+  float* lse_s;  // their log-sum-exps [Nq*(k-1) + 1][H_q]
   int64_t max_items;
   size_t bytes;
 };
@@ -131,8 +131,9 @@ AttnWs attn_layout(void* ws, int64_t q_start, int64_t Nq, int H_q, int H_kv, int
   w.max_items = msa::attn_max_items((int64_t)H_kv * nblk, nnz, (int)g_opt_chunk);
   w.items = c.take<int4>(sizeof(int4) * (size_t)w.max_items);
   w.n_items = c.take<int32_t>(2 * sizeof(int32_t));  // count, fetch counter
-  w.Os = c.take<void>(2 * (size_t)Nq * (k - 1) * H_q * d_h);
-  w.lse_s = c.take<float>(sizeof(float) * (size_t)Nq * (k - 1) * H_q);
+  // Nq * (k-1) slots plus one spare that rows past a work item's end write.
+  w.Os = c.take<void>(2 * ((size_t)Nq * (k - 1) + 1) * H_q * d_h);
+  w.lse_s = c.take<float>(sizeof(float) * ((size_t)Nq * (k - 1) + 1) * H_q);
   w.bytes = c.off;
   return w;
 }
@@ -155,7 +156,7 @@ msa_status run_attn(const void* Q, const void* K, const void* V, const int32_t* 
                              "work-list launch");
   if (st) return st;
   st = hip_status(msa::launch_attn(Q, K, V, col, slot, w.items, w.n_items, w.max_items, q_start,
-                                   Nk, H_q, H_kv, d_h, nblk, k, scale, w.Os, w.lse_s, s),
+                                   Nq, Nk, H_q, H_kv, d_h, nblk, k, scale, w.Os, w.lse_s, s),
                   "attention launch");
   if (st) return st;
   return hip_status(msa::launch_combine(Q, K, V, w.Os, w.lse_s, q_start, Nq, Nk, H_q, H_kv, d_h,

@@ -32,8 +32,8 @@ hipError_t launch_build_items(const int32_t* row_ptr, int64_t nb, int nblk, int6
                               hipStream_t stream);
 hipError_t launch_attn(const void* Q, const void* K, const void* V, const int32_t* col,
                        const uint8_t* slot, const int4* items, int32_t* n_items,
-                       int64_t max_items, int64_t q_start, int64_t Nk, int H_q, int H_kv,
-                       int d_h, int nblk, int k, float scale, void* Os, float* lse_s,
+                       int64_t max_items, int64_t q_start, int64_t Nq, int64_t Nk, int H_q,
+                       int H_kv, int d_h, int nblk, int k, float scale, void* Os, float* lse_s,
                        hipStream_t stream);
 hipError_t launch_combine(const void* Q, const void* K, const void* V, const void* Os,
                           const float* lse_s, int64_t q_start, int64_t Nq, int64_t Nk, int H_q,
