@@ -98,6 +98,11 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
     lstore(0, nxt);
   }
   __syncthreads();
+  // Settle every load issued so far (the query operand included) before the
+  // loop: the loads above sit on lane- and tile-dependent paths, and a load
+  // that might still be in flight at the loop head would make each block's
+  // first MFMA wait for the next block's prefetch as well.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // The sink takes block kb-1's pooled score while block kb's MFMAs are in
   // flight, so its VALU work can issue under them.
