@@ -141,30 +141,44 @@ __device__ __forceinline__ int k_swz(int row) {
 }
 
 // K and V of block (group r, keys key0..key0+127); keys >= Nk read as 0.
+// Every global load is issued before the first LDS store, so the block
+// arrives in one memory round trip.
 template <int DH>
 __device__ __forceinline__ void stage_kv(AttnSmem<DH>& sm, const __bf16* __restrict__ K,
                                          const __bf16* __restrict__ V, int r, int H_kv,
                                          int64_t key0, int64_t Nk, int t) {
-  constexpr int CH = DH / 8;  // 16-byte chunks per K row
-  for (int id = t; id < kBlock * CH; id += 256) {
-    const int row = id / CH, c = id % CH;
-    bf16x8 v = {};
-    if (key0 + row < Nk)
-      v = *reinterpret_cast<const bf16x8*>(K + ((key0 + row) * H_kv + r) * DH + 8 * c);
-    *reinterpret_cast<bf16x8*>(&sm.k[row * DH + 8 * (c ^ k_swz<DH>(row))]) = v;
-  }
-  for (int id = t; id < (kBlock / 4) * CH; id += 256) {
-    const int kq = id % (kBlock / 4), c = id / (kBlock / 4);  // 4 keys x 8 d
-    bf16x8 rows[4];
+  constexpr int CH = DH / 8;                   // 16-byte chunks per K row
+  constexpr int KL = kBlock * CH / 256;        // K chunks per thread
+  constexpr int VL = (kBlock / 4) * CH / 256;  // V (4 keys x 8 d) pieces per thread
+  bf16x8 kr[KL], vr[VL][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t key = key0 + 4 * kq + u;
-      rows[u] = key < Nk ? *reinterpret_cast<const bf16x8*>(V + (key * H_kv + r) * DH + 8 * c)
-                         : bf16x8{};
+  for (int u = 0; u < KL; ++u) {
+    const int id = t + 256 * u, row = id / CH, c = id % CH;
+    kr[u] = key0 + row < Nk
+                ? *reinterpret_cast<const bf16x8*>(K + ((key0 + row) * H_kv + r) * DH + 8 * c)
+                : bf16x8{};
+  }
+#pragma unroll
+  for (int u = 0; u < VL; ++u) {
+    const int id = t + 256 * u, kq = id % (kBlock / 4), c = id / (kBlock / 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t key = key0 + 4 * kq + e;
+      vr[u][e] = key < Nk ? *reinterpret_cast<const bf16x8*>(V + (key * H_kv + r) * DH + 8 * c)
+                          : bf16x8{};
     }
+  }
+#pragma unroll
+  for (int u = 0; u < KL; ++u) {
+    const int id = t + 256 * u, row = id / CH, c = id % CH;
+    *reinterpret_cast<bf16x8*>(&sm.k[row * DH + 8 * (c ^ k_swz<DH>(row))]) = kr[u];
+  }
+#pragma unroll
+  for (int u = 0; u < VL; ++u) {
+    const int id = t + 256 * u, kq = id % (kBlock / 4), c = id / (kBlock / 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      bf16x4 w = {rows[0][e], rows[1][e], rows[2][e], rows[3][e]};
+      bf16x4 w = {vr[u][0][e], vr[u][1][e], vr[u][2][e], vr[u][3][e]};
       *reinterpret_cast<bf16x4*>(&sm.vt[vt_off(8 * c + e, 4 * kq)]) = w;
     }
   }
@@ -399,14 +413,20 @@ __global__ __launch_bounds__(256, 2) void attn_kv_outer_kernel(
     const int4 it = items[item_id];
     const int bucket = it.x, start = it.y, count = it.z;
     const int r = bucket / nblk, b = bucket % nblk;
-    for (int p = t; p < count; p += 256) {
+    // Per-thread addresses are rebuilt for every item from a thread index
+    // the compiler cannot see through: hoisted out of this loop they would
+    // be spilled, and each reload would wait for every load in flight.
+    int tl = t;
+    asm volatile("" : "+v"(tl));
+    for (int p = tl; p < count; p += 256) {
       sm.pos[p] = col[start + p];
       sm.sl[p] = slot[start + p];
     }
-    stage_kv<DH>(sm, K, V, r, H_kv, (int64_t)b * kBlock, Nk, t);
+    stage_kv<DH>(sm, K, V, r, H_kv, (int64_t)b * kBlock, Nk, tl);
     __syncthreads();
+    const int ll = tl & 63;
     attn_item<DH>(sm, Q, count * G, wave, r, G, inv_G, H_q, H_kv, k, q_start, spare,
-                  scale_log2, Os, lse_s, lane >> 5, lane & 31);
+                  scale_log2, Os, lse_s, ll >> 5, ll & 31);
     __syncthreads();  // LDS and `next` are reused by the next item
   }
 }

@@ -79,46 +79,119 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const __bf16* __restri
   }
 }
 
-// (3) Partial attention of G heads over one selected block.
+// (3) Partial attention of the G heads of group r over one selected block:
+// one work-group per (sequence, group, selected block).  The block's K and V
+// are staged in LDS with coalesced 16-byte loads (K rows XOR-swizzled by
+// 16-byte chunk, so 16 lanes reading 16 consecutive rows at one chunk hit
+// distinct banks), q in fp32.  Scores: thread (key = t % 128, half = t / 128)
+// takes heads half, half + 2, ...; softmax: one wave per head; PV: thread
+// (d pair, head group) accumulates up to four heads per pass, reading each
+// V pair once for all of them.
+template <int DH>
+__device__ __forceinline__ int dk_swz(int row) {
+  return DH == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
 template <int DH>
 __global__ __launch_bounds__(256) void decode_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ sel, int64_t N, int H_q, int H_kv, int k, float scale_log2,
     float* __restrict__ Opart, float* __restrict__ lse_part) {
-  extern __shared__ float sm[];  // q [G][DH] fp32, s [G][128] fp32
+  constexpr int CH = DH / 8;            // 16-byte chunks per row
+  constexpr int LD = kBlock * CH / 256;  // chunks of K (and of V) per thread
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  __bf16* ks = reinterpret_cast<__bf16*>(dsm);           // [128][DH], swizzled
+  __bf16* vs = ks + kBlock * DH;                           // [128][DH]
+  float* qs = reinterpret_cast<float*>(vs + kBlock * DH);  // [G][DH]
   const int s_id = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   const int G = H_q / H_kv;
+  // Scores [G][128] fp32: over K once K is scored when one pass covers every
+  // head (G <= 16), else after q.
+  constexpr int HB = 8;  // heads per scoring pass per thread (two thread halves)
+  const bool alias = G <= 2 * HB;
+  float* ss = alias ? reinterpret_cast<float*>(dsm) : qs + G * DH;
   const int32_t blk = sel[((int64_t)b * H_kv + r) * k + s_id];
   if (blk < 0) return;
-  float* qs = sm;
-  float* ss = sm + G * DH;
   const int t = threadIdx.x;
-  for (int e = t; e < G * DH; e += 256)
-    qs[e] = bf2f(q[((int64_t)b * H_q + r * G) * DH + e]);
-  __syncthreads();
   const int64_t key0 = (int64_t)blk * kBlock;
-  const __bf16* Kb = K + ((int64_t)b * N) * H_kv * DH;
-  const __bf16* Vb = V + ((int64_t)b * N) * H_kv * DH;
-  // scores: (head, key) pairs
-  for (int e = t; e < G * kBlock; e += 256) {
-    const int hh = e / kBlock, key = e % kBlock;
-    const int64_t j = key0 + key;
-    float s = -INFINITY;
-    if (j < N) {
-      const __bf16* kr = Kb + (j * H_kv + r) * DH;
-      const float* qr = qs + hh * DH;
-      s = 0.f;
-      for (int v = 0; v < DH / 8; ++v) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(kr + 8 * v);
+  const __bf16* Kb = K + (int64_t)b * N * H_kv * DH;
+  const __bf16* Vb = V + (int64_t)b * N * H_kv * DH;
+  {
+    // every load of the block is issued before the first LDS store
+    bf16x8 kx[LD], vx[LD];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) s = fmaf(qr[8 * v + u], bf2f(x[u]), s);
+    for (int u = 0; u < LD; ++u) {
+      const int id = t + 256 * u, row = id / CH, c = id % CH;
+      const int64_t j = key0 + row;
+      kx[u] = vx[u] = bf16x8{};
+      if (j < N) {
+        kx[u] = *reinterpret_cast<const bf16x8*>(Kb + (j * H_kv + r) * DH + 8 * c);
+        vx[u] = *reinterpret_cast<const bf16x8*>(Vb + (j * H_kv + r) * DH + 8 * c);
       }
-      s *= scale_log2;
     }
-    ss[hh * kBlock + key] = s;
+#pragma unroll
+    for (int u = 0; u < LD; ++u) {
+      const int id = t + 256 * u, row = id / CH, c = id % CH;
+      *reinterpret_cast<bf16x8*>(ks + row * DH + 8 * (c ^ dk_swz<DH>(row))) = kx[u];
+      *reinterpret_cast<bf16x8*>(vs + row * DH + 8 * c) = vx[u];
+    }
+  }
+  for (int e = t; e < G * CH; e += 256) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(q + ((int64_t)b * H_q + r * G) * DH + 8 * e);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) qs[8 * e + u] = bf2f(x[u]);
   }
   __syncthreads();
-  // softmax per head (one wave per head at a time), probabilities in place
+
+  // ---- scores ----------------------------------------------------------------
+  {
+    const int key = t & (kBlock - 1), half = t >> 7;
+    const bool valid = key0 + key < N;
+    float sc[HB];
+    for (int h0 = half; h0 < G; h0 += 2 * HB) {
+#pragma unroll
+      for (int j = 0; j < HB; ++j) sc[j] = 0.f;
+      for (int c = 0; c < CH; ++c) {
+        const bf16x8 kx =
+            *reinterpret_cast<const bf16x8*>(ks + key * DH + 8 * (c ^ dk_swz<DH>(key)));
+        float kf[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kf[u] = bf2f(kx[u]);
+#pragma unroll
+        for (int j = 0; j < HB; ++j) {
+          const int h = h0 + 2 * j;
+          if (h < G) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(qs + h * DH + 8 * c);
+            const f32x4 d = *reinterpret_cast<const f32x4*>(qs + h * DH + 8 * c + 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              sc[j] = fmaf(a[u], kf[u], sc[j]);
+              sc[j] = fmaf(d[u], kf[4 + u], sc[j]);
+            }
+          }
+        }
+      }
+      if (!alias) {
+#pragma unroll
+        for (int j = 0; j < HB; ++j) {
+          const int h = h0 + 2 * j;
+          if (h < G) ss[h * kBlock + key] = valid ? sc[j] * scale_log2 : -INFINITY;
+        }
+      }
+    }
+    if (alias) {  // one pass: wait until every thread is done reading K
+      __syncthreads();
+      if (half < G) {
+#pragma unroll
+        for (int j = 0; j < HB; ++j) {
+          const int h = half + 2 * j;
+          if (h < G) ss[h * kBlock + key] = valid ? sc[j] * scale_log2 : -INFINITY;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // ---- softmax per head (one wave per head), probabilities in place --------
   const int wave = t >> 6, lane = t & 63;
   for (int hh = wave; hh < G; hh += 4) {
     float* row = ss + hh * kBlock;
@@ -132,16 +205,46 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
       lse_part[(((int64_t)b * H_q + r * G + hh) * k) + s_id] = (m + log2f(l)) * 0.69314718055994531f;
   }
   __syncthreads();
-  // O_s[h][d] = sum_key p[h][key] V[key][d]
-  for (int e = t; e < G * DH; e += 256) {
-    const int hh = e / DH, d = e % DH;
-    const float* p = ss + hh * kBlock;
-    float acc = 0.f;
-    for (int key = 0; key < kBlock; ++key) {
-      const int64_t j = key0 + key;
-      if (j < N) acc = fmaf(p[key], bf2f(Vb[(j * H_kv + r) * DH + d]), acc);
+  // ---- O_s[h][d] = sum_key p[h][key] V[key][d] -------------------------------
+  {
+    constexpr int NDP = DH / 2;      // d pairs
+    constexpr int NHG = 256 / NDP;   // head groups
+    constexpr int HP = 4;            // heads per pass per thread
+    const int dp = t % NDP, hg = t / NDP;
+    for (int h0 = hg; h0 < G; h0 += NHG * HP) {
+      float a0[HP], a1[HP];
+#pragma unroll
+      for (int j = 0; j < HP; ++j) a0[j] = a1[j] = 0.f;
+      for (int key = 0; key < kBlock; key += 4) {
+        float v0[4], v1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(vs + (key + u) * DH + 2 * dp);
+          v0[u] = __uint_as_float(w << 16);
+          v1[u] = __uint_as_float(w & 0xffff0000u);
+        }
+#pragma unroll
+        for (int j = 0; j < HP; ++j) {
+          const int h = h0 + NHG * j;
+          if (h < G) {
+            const f32x4 p = *reinterpret_cast<const f32x4*>(ss + h * kBlock + key);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              a0[j] = fmaf(p[u], v0[u], a0[j]);
+              a1[j] = fmaf(p[u], v1[u], a1[j]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < HP; ++j) {
+        const int h = h0 + NHG * j;
+        if (h < G) {
+          float* dst = Opart + (((int64_t)b * H_q + r * G + h) * k + s_id) * DH + 2 * dp;
+          *reinterpret_cast<float2*>(dst) = float2{a0[j], a1[j]};
+        }
+      }
     }
-    Opart[(((int64_t)b * H_q + r * G + hh) * k + s_id) * DH + d] = acc;
   }
 }
 
@@ -195,7 +298,20 @@ hipError_t launch_decode_attn(const void* q, const void* K, const void* V, const
   const int G = H_q / H_kv;
   const float scale_log2 = scale * 1.4426950408889634f;
   dim3 grid(k, H_kv, B), block(256);
-  const size_t lds = sizeof(float) * (size_t)G * (d_h + kBlock);
+  // K, V, q and (when they do not go over K) the scores
+  const size_t lds = 2 * sizeof(__bf16) * kBlock * d_h + sizeof(float) * (size_t)G * d_h +
+                     (G <= 16 ? 0 : sizeof(float) * (size_t)G * kBlock);
+  static bool lds_ready = false;  // up to 128 KiB (G = 64): above the default 64 KiB
+  if (!lds_ready) {
+    const size_t most = 2 * sizeof(__bf16) * kBlock * 128 + sizeof(float) * 64 * (128 + kBlock);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attn_kernel<128>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attn_kernel<64>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
+    if (e != hipSuccess) return e;
+    lds_ready = true;
+  }
   auto* qq = static_cast<const __bf16*>(q);
   auto* kk = static_cast<const __bf16*>(K);
   auto* vv = static_cast<const __bf16*>(V);

@@ -327,9 +327,21 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ prow, int lb,
   uint64_t lst[LM];
 #pragma unroll
   for (int j = 0; j < LM; ++j) lst[j] = 0;  // below every real key
-  for (int b = lane; b < lb; b += kWave) {
-    const uint64_t key = ((uint64_t)ord_f32(prow[b]) << 32) | (uint32_t)(~b);
-    if (key > lst[LM - 1]) list_insert<LM>(lst, key);
+  // Scores are read eight per lane at a time, so the loads of a batch are in
+  // flight together.
+  for (int b0 = 0; b0 < lb; b0 += 8 * kWave) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = b0 + kWave * u + lane;
+      v[u] = b < lb ? prow[b] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = b0 + kWave * u + lane;
+      const uint64_t key = ((uint64_t)ord_f32(v[u]) << 32) | (uint32_t)(~b);
+      if (b < lb && key > lst[LM - 1]) list_insert<LM>(lst, key);
+    }
   }
   int mine = lb;  // lane K1 keeps the local block
   for (int p = 0; p < K1; ++p) {

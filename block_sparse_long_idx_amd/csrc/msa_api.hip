@@ -140,6 +140,8 @@ AttnWs attn_layout(void* ws, int64_t q_start, int64_t Nq, int H_q, int H_kv, int
 
 msa_status check_attn_shapes(int H_q, int H_kv, int d_h) {
   if (H_q < 1 || H_q % H_kv) return fail(MSA_ERR_INVALID_ARG, "H_q must be a positive multiple of H_kv");
+  if (H_q / H_kv > 64)
+    return fail(MSA_ERR_UNSUPPORTED, "at most 64 query heads per KV head (got %d)", H_q / H_kv);
   if (d_h != 64 && d_h != 128) return fail(MSA_ERR_UNSUPPORTED, "d_h must be 64 or 128 (got %d)", d_h);
   return MSA_OK;
 }

@@ -35,8 +35,9 @@
  * kept per thread and read with msa_last_error().
  *
  * Supported shapes: B_k = 128; d_h in {64, 128}; d_idx in {32, 64, 128};
- * 1 <= k <= 32; H_q a multiple of H_kv; H_kv <= 64; every block count
- * ceil(N / B_k) <= 16384; every selection nnz < 2^31.
+ * 1 <= k <= 32; H_q a multiple of H_kv with G = H_q / H_kv <= 64;
+ * H_kv <= 64; every block count ceil(N / B_k) <= 16384; every selection
+ * nnz < 2^31.
  *
  * Determinism: every output is bitwise identical from run to run.
  */

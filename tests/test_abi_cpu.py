@@ -81,6 +81,9 @@ def test_attn_rejects(lib):
     # d_h unsupported
     assert lib.msa_sparse_attn_fwd(*base, 0, 128, 128, 8, 4, 96, 128, 4, 0.1, FAKE, NULL,
                                    FAKE, 1 << 30, NULL) == msa.ERR_UNSUPPORTED
+    # more than 64 query heads per KV head
+    assert lib.msa_sparse_attn_fwd(*base, 0, 128, 128, 130, 2, 128, 128, 4, 0.1, FAKE, NULL,
+                                   FAKE, 1 << 30, NULL) == msa.ERR_UNSUPPORTED
     # bad scale
     assert lib.msa_sparse_attn_fwd(*base, 0, 128, 128, 8, 4, 128, 128, 4, -1.0, FAKE, NULL,
                                    FAKE, 1 << 30, NULL) == msa.ERR_INVALID_ARG
@@ -101,6 +104,8 @@ def test_prefill_and_decode_reject(lib):
                           FAKE, 1 << 30, NULL) == msa.ERR_UNSUPPORTED   # H_kv * d_idx = 192 does not divide 512
     assert lib.msa_decode(*five, 0, 1024, 8, 4, 128, 64, 128, 4, 0.1, FAKE, FAKE, NULL,
                           FAKE, 1 << 30, NULL) == msa.ERR_INVALID_ARG
+    assert lib.msa_decode(*five, 2, 1024, 65, 1, 128, 64, 128, 4, 0.1, FAKE, FAKE, NULL,
+                          FAKE, 1 << 30, NULL) == msa.ERR_UNSUPPORTED   # G = 65
 
 
 def test_options(lib):
