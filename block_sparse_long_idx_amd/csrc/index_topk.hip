@@ -16,8 +16,8 @@ namespace msa {
 //
 // Work-group = (group r, tile of 256 query positions); 4 waves x 64 queries.
 // The WG sweeps key blocks kb = 0 .. lb(last query)-1 in ascending order:
-// each block's 128 index keys are staged once in LDS (double-buffered) and
-// shared by the 4 waves.  A wave computes S^T = K_blk . Q^T with keys as
+// each block's 128 index keys are copied once into LDS by direct
+// global->LDS loads (double-buffered) and shared by the 4 waves.  A wave computes S^T = K_blk . Q^T with keys as
 // MFMA rows and its queries as columns, so every lane's 16 accumulators are
 // 16 keys of one query: the 128-key max is an in-lane max plus one swap
 // between the two lane halves.  Only blocks strictly before a query's local
@@ -48,7 +48,6 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
                                             __bf16 (*lds)[128 * D], Sink& sink) {
   constexpr int S = D / 16;   // MFMA k-steps
   constexpr int CH = D / 8;   // 16-byte chunks per key row
-  constexpr int LOADS = 128 * CH / 256;
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int h = lane >> 5, n = lane & 31;
@@ -74,35 +73,27 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
     }
   }
 
-  auto gload = [&](int kb, bf16x8 (&regs)[LOADS]) {
+  // Key block kb -> LDS buffer `buf` by direct global->LDS loads (no
+  // registers): each wave-instruction fills one contiguous KiB, lane i
+  // writing bytes 16i..16i+15, i.e. key rows v*RPI .. v*RPI+RPI-1; a lane
+  // fetches the global chunk that the swizzled layout keeps at its LDS spot.
+  constexpr int RPI = 1024 / (2 * D);      // key rows per wave-instruction
+  constexpr int PER_WAVE = 128 / RPI / 4;  // wave-instructions per wave per block
+  auto dma = [&](int kb, int buf) {
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int id = t + 256 * u;
-      const int row = id / CH, c = id % CH;
-      regs[u] = *reinterpret_cast<const bf16x8*>(
-          k_idx + (((int64_t)kb * kBlock + row) * H_kv + r) * D + 8 * c);
+    for (int u = 0; u < PER_WAVE; ++u) {
+      const int v = wave * PER_WAVE + u;
+      const int row = v * RPI + lane / CH, cs = lane % CH;
+      const __bf16* src =
+          k_idx + (((int64_t)kb * kBlock + row) * H_kv + r) * D + 8 * (cs ^ kswz<D>(row));
+      __builtin_amdgcn_global_load_lds(src, &lds[buf][v * 512], 16, 0, 0);
     }
   };
-  auto lstore = [&](int buf, const bf16x8 (&regs)[LOADS]) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int id = t + 256 * u;
-      const int row = id / CH, c = id % CH;
-      *reinterpret_cast<bf16x8*>(&lds[buf][row * D + 8 * (c ^ kswz<D>(row))]) = regs[u];
-    }
-  };
-
-  bf16x8 nxt[LOADS];
-  if (kb_end > 0) {
-    gload(0, nxt);
-    lstore(0, nxt);
-  }
+  // Two buffers: block kb+1 is fetched while block kb is scored.  (A third
+  // buffer, fetching two blocks ahead, measured no faster.)
+  if (kb_end > 0) dma(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // block 0 and the query operand
   __syncthreads();
-  // Settle every load issued so far (the query operand included) before the
-  // loop: the loads above sit on lane- and tile-dependent paths, and a load
-  // that might still be in flight at the loop head would make each block's
-  // first MFMA wait for the next block's prefetch as well.
-  __builtin_amdgcn_s_waitcnt(0);
 
   // The sink takes block kb-1's pooled score while block kb's MFMAs are in
   // flight, so its VALU work can issue under them.
@@ -110,7 +101,7 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
   float v_prev = -INFINITY;
   for (int kb = 0; kb < kb_end; ++kb) {
     const int buf = kb & 1;
-    if (kb + 1 < kb_end) gload(kb + 1, nxt);
+    if (kb + 1 < kb_end) dma(kb + 1, buf ^ 1);
     if (kb < kb_end_w) {
       float m0 = -INFINITY, m1 = -INFINITY;
       // key-row groups in pairs: the second group's MFMAs overlap the first
@@ -147,7 +138,7 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
       kb_prev = kb;
       v_prev = h ? m1 : m0;
     }
-    if (kb + 1 < kb_end) lstore(buf ^ 1, nxt);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of block kb+1 is in LDS
     __syncthreads();
   }
   if (kb_prev >= 0) sink(kb_prev, kb_end_w, v_prev);
