@@ -14,7 +14,9 @@ namespace msa {
 // ---------------------------------------------------------------------------
 // Score GEMM + block max-pool.
 //
-// Work-group = (group r, tile of 256 query positions); 4 waves x 64 queries.
+// Work-group = (group r, tile of 64*NW query positions); NW = 4 or 8 waves
+// x 64 queries (8 when the grid still fills the chip: each staged key block
+// then serves twice the queries).
 // The WG sweeps key blocks kb = 0 .. lb(last query)-1 in ascending order:
 // each block's 128 index keys are copied once into LDS by direct
 // global->LDS loads (double-buffered) and shared by the 4 waves.  A wave computes S^T = K_blk . Q^T with keys as
@@ -41,7 +43,7 @@ __device__ __forceinline__ int kswz(int row) {
 // The sweep shared by both Index-Branch variants.  For every key block kb
 // it hands the pooled score of the lane's own query to `sink(kb, v)`; the
 // lane owns query q_own = qw0 + 32*h + n (lane half h <-> column group h).
-template <int D, typename Sink>
+template <int D, int NW, typename Sink>
 __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
                                             const __bf16* __restrict__ k_idx, int64_t q_start,
                                             int64_t Nq, int H_kv, int r, int tile,
@@ -52,9 +54,9 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
   const int wave = t >> 6, lane = t & 63;
   const int h = lane >> 5, n = lane & 31;
   const int64_t q_end = q_start + Nq;
-  const int64_t q0 = q_start + (int64_t)tile * 256;
+  const int64_t q0 = q_start + (int64_t)tile * (64 * NW);
   const int64_t qw0 = q0 + wave * 64;
-  const int64_t q_last = min(q0 + 255, q_end - 1);
+  const int64_t q_last = min(q0 + 64 * NW - 1, q_end - 1);
   const int kb_end = (int)(q_last / kBlock);
   const int kb_end_w = qw0 < q_end ? (int)(min(qw0 + 63, q_end - 1) / kBlock) : 0;
 
@@ -78,7 +80,7 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
   // writing bytes 16i..16i+15, i.e. key rows v*RPI .. v*RPI+RPI-1; a lane
   // fetches the global chunk that the swizzled layout keeps at its LDS spot.
   constexpr int RPI = 1024 / (2 * D);      // key rows per wave-instruction
-  constexpr int PER_WAVE = 128 / RPI / 4;  // wave-instructions per wave per block
+  constexpr int PER_WAVE = 128 / RPI / NW;  // wave-instructions per wave per block
   auto dma = [&](int kb, int buf) {
 #pragma unroll
     for (int u = 0; u < PER_WAVE; ++u) {
@@ -182,8 +184,8 @@ struct PoolStore {
   }
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void index_pool_kernel(
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void index_pool_kernel(
     const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx,
     int64_t q_start, int64_t Nq, int H_kv, int ntiles, float* __restrict__ P,
     int64_t ldp) {
@@ -191,11 +193,11 @@ __global__ __launch_bounds__(256) void index_pool_kernel(
   int r, tile;
   if (!index_tile_of(blockIdx.x, ntiles, H_kv, r, tile)) return;
   const int lane = threadIdx.x & 63;
-  const int64_t q_own = q_start + (int64_t)tile * 256 + (threadIdx.x >> 6) * 64 +
+  const int64_t q_own = q_start + (int64_t)tile * (64 * NW) + (threadIdx.x >> 6) * 64 +
                         32 * (lane >> 5) + (lane & 31);
   PoolStore sink{P + ((int64_t)r * Nq + (q_own - q_start)) * ldp, q_own < q_start + Nq,
                  {0.f, 0.f, 0.f, 0.f}};
-  index_sweep<D>(q_idx, k_idx, q_start, Nq, H_kv, r, tile, lds, sink);
+  index_sweep<D, NW>(q_idx, k_idx, q_start, Nq, H_kv, r, tile, lds, sink);
 }
 
 // Sink of the fused variant: a running Top-LM list of (score, block) per
@@ -224,15 +226,15 @@ struct TopkKeep {
   }
 };
 
-template <int D, int LM>
-__global__ __launch_bounds__(256) void index_topk_fused_kernel(
+template <int D, int NW, int LM>
+__global__ __launch_bounds__(64 * NW) void index_topk_fused_kernel(
     const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx, int64_t q_start,
     int64_t Nq, int H_kv, int ntiles, int k, int32_t* __restrict__ sel) {
   __shared__ __attribute__((aligned(16))) __bf16 lds[2][128 * D];
   int r, tile;
   if (!index_tile_of(blockIdx.x, ntiles, H_kv, r, tile)) return;
   const int lane = threadIdx.x & 63;
-  const int64_t q_own = q_start + (int64_t)tile * 256 + (threadIdx.x >> 6) * 64 +
+  const int64_t q_own = q_start + (int64_t)tile * (64 * NW) + (threadIdx.x >> 6) * 64 +
                         32 * (lane >> 5) + (lane & 31);
   const bool own_ok = q_own < q_start + Nq;
   TopkKeep<LM> keep;
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(256) void index_topk_fused_kernel(
     keep.sc[j] = -INFINITY;
     keep.bk[j] = -1;
   }
-  index_sweep<D>(q_idx, k_idx, q_start, Nq, H_kv, r, tile, lds, keep);
+  index_sweep<D, NW>(q_idx, k_idx, q_start, Nq, H_kv, r, tile, lds, keep);
   if (!own_ok) return;
   int32_t* out = sel + ((q_own - q_start) * H_kv + r) * k;
   const int K1 = k - 1, lb = keep.lb_own;
@@ -263,25 +265,40 @@ __global__ __launch_bounds__(256) void index_topk_fused_kernel(
   out[K1] = lb;
 }
 
+// Waves per index work-group: 8 when 512-query tiles still give at least
+// one work-group per CU, else 4.  d_idx = 128 keeps 4: its accumulators and
+// query operand need more registers than two waves per SIMD leave.
+static int index_waves(int64_t Nq, int H_kv, int d_idx) {
+  return d_idx < 128 && ceil_div(Nq, (int64_t)512) * H_kv >= device_cus() ? 8 : 4;
+}
+
+template <int D, int NW>
+static void launch_pool_dn(const __bf16* qi, const __bf16* ki, int64_t q_start, int64_t Nq,
+                           int H_kv, float* P, int64_t ldp, hipStream_t stream) {
+  const int ntiles = (int)ceil_div(Nq, (int64_t)(64 * NW));
+  index_pool_kernel<D, NW><<<index_grid(ntiles, H_kv), 64 * NW, 0, stream>>>(
+      qi, ki, q_start, Nq, H_kv, ntiles, P, ldp);
+}
+
+template <int D>
+static void launch_pool_d(const __bf16* qi, const __bf16* ki, int64_t q_start, int64_t Nq,
+                          int H_kv, float* P, int64_t ldp, hipStream_t stream) {
+  if (D < 128 && index_waves(Nq, H_kv, D) == 8)
+    launch_pool_dn<D, D < 128 ? 8 : 4>(qi, ki, q_start, Nq, H_kv, P, ldp, stream);
+  else
+    launch_pool_dn<D, 4>(qi, ki, q_start, Nq, H_kv, P, ldp, stream);
+}
+
 hipError_t launch_index_pool(const void* q_idx, const void* k_idx, int64_t q_start,
                              int64_t Nq, int H_kv, int d_idx, float* P, int64_t ldp,
                              hipStream_t stream) {
-  const int ntiles = (int)ceil_div(Nq, 256);
-  dim3 grid(index_grid(ntiles, H_kv)), block(256);
   auto* qi = static_cast<const __bf16*>(q_idx);
   auto* ki = static_cast<const __bf16*>(k_idx);
   switch (d_idx) {
-    case 32:
-      index_pool_kernel<32><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, P, ldp);
-      break;
-    case 64:
-      index_pool_kernel<64><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, P, ldp);
-      break;
-    case 128:
-      index_pool_kernel<128><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, P, ldp);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 32: launch_pool_d<32>(qi, ki, q_start, Nq, H_kv, P, ldp, stream); break;
+    case 64: launch_pool_d<64>(qi, ki, q_start, Nq, H_kv, P, ldp, stream); break;
+    case 128: launch_pool_d<128>(qi, ki, q_start, Nq, H_kv, P, ldp, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -400,17 +417,26 @@ hipError_t launch_topk_decode(const float* P, int64_t ldp, int B, int H_kv, int 
   return launch_topk(P, ldp, (int64_t)B * H_kv, 1, H_kv, 0, nblk, k, sel, stream);
 }
 
+template <int D, int NW>
+static void launch_fused_dn(const __bf16* qi, const __bf16* ki, int64_t q_start, int64_t Nq,
+                            int H_kv, int k, int32_t* sel, hipStream_t stream) {
+  const int ntiles = (int)ceil_div(Nq, (int64_t)(64 * NW));
+  dim3 grid(index_grid(ntiles, H_kv)), block(64 * NW);
+  if (k <= 8)
+    index_topk_fused_kernel<D, NW, 7><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
+  else if (k <= 16)
+    index_topk_fused_kernel<D, NW, 15><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
+  else
+    index_topk_fused_kernel<D, NW, 31><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
+}
+
 template <int D>
 static void launch_fused_d(const __bf16* qi, const __bf16* ki, int64_t q_start, int64_t Nq,
                            int H_kv, int k, int32_t* sel, hipStream_t stream) {
-  const int ntiles = (int)ceil_div(Nq, 256);
-  dim3 grid(index_grid(ntiles, H_kv)), block(256);
-  if (k <= 8)
-    index_topk_fused_kernel<D, 7><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
-  else if (k <= 16)
-    index_topk_fused_kernel<D, 15><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
+  if (D < 128 && index_waves(Nq, H_kv, D) == 8)
+    launch_fused_dn<D, D < 128 ? 8 : 4>(qi, ki, q_start, Nq, H_kv, k, sel, stream);
   else
-    index_topk_fused_kernel<D, 31><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
+    launch_fused_dn<D, 4>(qi, ki, q_start, Nq, H_kv, k, sel, stream);
 }
 
 hipError_t launch_index_topk_fused(const void* q_idx, const void* k_idx, int64_t q_start,

@@ -7,6 +7,9 @@
 
 namespace msa {
 
+// attn.hip: compute units of the current device (cached per device)
+int device_cus();
+
 // index_topk.hip
 hipError_t launch_index_pool(const void* q_idx, const void* k_idx, int64_t q_start, int64_t Nq,
                              int H_kv, int d_idx, float* P, int64_t ldp, hipStream_t stream);

@@ -56,6 +56,9 @@ STAGE_CASES = [
     (5000, 6, 2, 128, 64, 32, 4, 0, 5000),      # k = 32, G = 3
     (777, 2, 2, 64, 32, 1, 0, 0, 777),          # k = 1: local block only
     (600, 64, 1, 128, 64, 3, 1, 0, 600),        # G = 64 (> 32 rows per position)
+    # H_kv = 64: enough 512-query tiles for the 8-wave Index work-groups
+    (2600, 64, 64, 64, 64, 8, 2, 0, 2600),
+    (3000, 64, 64, 64, 32, 16, 3, 333, 2667),   # d_idx 32, unaligned q_start
 ]
 
 
