@@ -436,13 +436,10 @@ __global__ __launch_bounds__(256, 2) void attn_kv_outer_kernel(
 // chunk's positions inside block b, times the G heads of group r, in 32-row
 // tiles.  Per tile: S^T over the block with the causal mask key <= i, P
 // split as hi + lo bf16 (two MFMAs, ~fp32 accuracy), O_loc and lse_loc in
-// registers; then the local block and the row's non-local partials (slots
-// 0 .. n_sel-2) are merged in a fixed order -- local block first, then the
-// non-local slots ascending:
+// registers; then the row's non-local partials (slots 0 .. n_sel-2) and the
+// local block (slot n_sel-1) are merged in ascending slot order:
 //   M = max lse, w_s = exp(lse_s - M), O = sum w_s O_s / sum w_s,
 //   lse = M + ln sum w_s.
-// Starting the sums with the local block lets its accumulators become the
-// running sum, which keeps the merge within the register budget.
 // ---------------------------------------------------------------------------
 template <int DH>
 __global__ __launch_bounds__(256, 2) void combine_local_kernel(
@@ -535,9 +532,8 @@ __global__ __launch_bounds__(256, 2) void combine_local_kernel(
     // ---- merge with the non-local partials ------------------------------------
     // nns = n_sel - 1 non-local slots (uniform over the work-group).  Their
     // lse values are requested together (addresses clamped to the row's
-    // last slot, so every load is in bounds and none is predicated), then
-    // the partials are accumulated two slots per round trip, in ascending
-    // slot order; the second slot of an odd tail gets weight 0.
+    // last slot, so every load is in bounds and none is predicated) for the
+    // max; the partials are then accumulated in ascending slot order.
     const int iq = row.pos - (int)q_start;
     const float lse_loc = (mb + log2f(l)) * 0.69314718055994531f;
     const int nns = n_sel - 1;
@@ -550,44 +546,39 @@ __global__ __launch_bounds__(256, 2) void combine_local_kernel(
 #pragma unroll
       for (int s = 0; s < kMaxK - 1; ++s) M = fmaxf(M, lv[s]);
     }
-    // Local block first: acc = w_loc * O_loc with O_loc = oacc / l.
-    const float w_loc = __expf(lse_loc - M);
-    const float wl = w_loc / l;
     float acc[NDG][16];
 #pragma unroll
     for (int dg = 0; dg < NDG; ++dg)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[dg][j] = wl * oacc[dg][j];
-    float den = w_loc;
+      for (int j = 0; j < 16; ++j) acc[dg][j] = 0.f;
+    float den = 0.f;
     const __bf16* src =
         Os + ((int64_t)iq * (k - 1) * H_kv + r) * (DH / 4) * G * 4 + (row.hq - r * G) * 4;
-    for (int s = 0; s < nns; s += 2) {
-      const int s1 = min(s + 1, nns - 1);
-      const float l0 = ls[s * H_q], l1 = ls[s1 * H_q];
-      const __bf16* p0 = src + (int64_t)s * (DH / 4) * H_q * 4;
-      const __bf16* p1 = src + (int64_t)s1 * (DH / 4) * H_q * 4;
-      bf16x4 x0[NDG][4], x1[NDG][4];
+    for (int s = 0; s < nns; ++s) {
+      const float w = __expf(ls[s * H_q] - M);
+      den += w;
+      const __bf16* ps = src + (int64_t)s * (DH / 4) * H_q * 4;
+      bf16x4 x[NDG][4];
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg)
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          x0[dg][qd] = *reinterpret_cast<const bf16x4*>(p0 + (8 * dg + 2 * qd + h) * G * 4);
-          x1[dg][qd] = *reinterpret_cast<const bf16x4*>(p1 + (8 * dg + 2 * qd + h) * G * 4);
-        }
-      const float w0 = __expf(l0 - M);
-      const float w1 = s + 1 < nns ? __expf(l1 - M) : 0.f;
-      den += w0;
-      den += w1;
+        for (int qd = 0; qd < 4; ++qd)
+          x[dg][qd] = *reinterpret_cast<const bf16x4*>(ps + (8 * dg + 2 * qd + h) * G * 4);
 #pragma unroll
       for (int dg = 0; dg < NDG; ++dg)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[dg][4 * qd + e] += w0 * bf2f(x0[dg][qd][e]);
-            acc[dg][4 * qd + e] += w1 * bf2f(x1[dg][qd][e]);
-          }
+          for (int e = 0; e < 4; ++e) acc[dg][4 * qd + e] += w * bf2f(x[dg][qd][e]);
     }
+    // the local block (the highest block id) last: O_loc = oacc / l
+    const float w_loc = __expf(lse_loc - M);
+    den += w_loc;
+    const float wl = w_loc / l;
+#pragma unroll
+    for (int dg = 0; dg < NDG; ++dg)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[dg][j] += wl * oacc[dg][j];
     const float inv = 1.f / den;
     float* dst = O + ((int64_t)iq * H_q + row.hq) * DH;
 #pragma unroll
