@@ -9,8 +9,8 @@ heads, 4 KV heads, d_h 128, d_idx 64, k 16, B_k 128, query chunks of 65,536.
 Prints one JSON line: prefill tokens/s (value), effective TFLOP/s by the
 MSA FLOP formula 4*H_q*d_h*N*k*B_k + H_kv*d_idx*N^2 (as a fraction of the
 2.5 PFLOP/s bf16 MFMA peak), per-stage times, the roofline of the dominant
-kernel, the CPU oracle timed on sampled rows, and 128K-prefill and
-32 x 1M decode figures.
+kernel, the CPU oracle timed on sampled rows, and the index-alignment KL
+pass, 128K-prefill and 32 x 1M decode figures.
 """
 import argparse
 import json
@@ -146,6 +146,48 @@ def time_prefill(cfg, t, steps, warmup):
     ms = start.elapsed_time(end) / steps
     st = [x / steps for x in pf.stage_ms()]
     return pf, ms, st
+
+
+def time_kl(pf, cfg, t, reps=2):
+    """The index-alignment KL pass (msa_index_kl) over every chunk of a step,
+    from the step's lse.  Each chunk's inverted index is rebuilt first (its
+    buffers are shared between chunks); only the KL calls are timed."""
+    import torch
+    msa = pf.msa
+    lib = msa.load()
+    ws = max(lib.msa_index_kl_workspace_bytes(q0, nq, cfg.H_kv, cfg.B_k, cfg.k)
+             for q0, nq in pf.chunks)
+    ws = torch.empty(ws, dtype=torch.uint8, device=t["Q"].device)
+    kl = torch.empty((cfg.N, cfg.H_kv), dtype=torch.float32, device=t["Q"].device)
+    sums = torch.empty(len(pf.chunks), dtype=torch.float64, device=t["Q"].device)
+    total_ms, nnz = 0.0, 0
+    for rep in range(reps + 1):
+        ms = 0.0
+        for c, (q0, nq) in enumerate(pf.chunks):
+            rp, col, slot = msa.invert_index(pf.sel[q0:q0 + nq], q_start=q0, ws=pf.ws_v,
+                                             row_ptr=pf.row_ptr, col=pf.col, slot=pf.slot)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            msa.index_kl(t["Q"], t["K"], t["q_idx"], t["k_idx"], pf.lse[q0:q0 + nq], rp, col,
+                         slot, cfg.k, q_start=q0, Nq=nq, scale=cfg.scale, kl=kl[q0:q0 + nq],
+                         kl_sum=sums[c:c + 1], ws=ws)
+            b.record()
+            b.synchronize()
+            ms += a.elapsed_time(b)
+            if rep == 0:
+                nnz += msa.selection_nnz(q0, nq, cfg.H_kv, cfg.k)
+        if rep > 0:
+            total_ms += ms
+    ms = total_ms / reps
+    G = cfg.H_q // cfg.H_kv
+    # per (query, group, selected block): the group's Q rows, q_idx, its lse
+    # values and the 12-byte partial
+    nbytes = nnz * (2 * G * cfg.d_h + 2 * cfg.d_idx + 4 * G + 12)
+    return {"ms_per_step": round(ms, 3),
+            "kl_mean": float(sums.sum().item() / (cfg.N * cfg.H_kv)),
+            "GB_per_s": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_per_step": nbytes}
 
 
 def cpu_baseline(cfg, t, n_rows):
@@ -295,10 +337,14 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on {args.cpu_rows} sampled rows")
         out["cpu_baseline"] = cpu_baseline(cfg, t, args.cpu_rows)
+    kl_leg = None
+    if not args.no_extra:
+        log("[bench] index KL leg")
+        kl_leg = time_kl(pf, cfg, t)
     del pf, t
     torch.cuda.empty_cache()
     if not args.no_extra:
-        extra = {}
+        extra = {f"index_kl_{cfg.name}": kl_leg}
         if cfg.name != "128k":
             c2 = CONFIGS["128k"]
             log("[bench] 128K prefill leg")

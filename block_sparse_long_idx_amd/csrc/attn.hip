@@ -27,6 +27,7 @@
 // heads of a position that one MFMA tile holds store G * 8 contiguous
 // bytes per instruction, and the combine reads them back the same way.
 #include "common.h"
+#include "lds_rows.h"
 #include "msa_internal.h"
 
 #include <algorithm>
@@ -36,18 +37,20 @@ namespace msa {
 // ---------------------------------------------------------------------------
 // Work list.  Bucket (r, b) of the CSR holds first the queries whose local
 // block is b (positions inside block b, all of which select it), then the
-// queries that picked b as a non-local block.  The first part is handled by
-// the combine; the second is cut into items of at most `chunk` positions.
-// Item = {bucket, start offset into col, count, 0}.
+// queries that picked b as a non-local block.  For the attention the first
+// part is handled by the combine and only the second is cut into items of
+// at most `chunk` positions; with `with_local` (the index KL pass) the
+// whole bucket is.  Item = {bucket, start offset into col, count, 0}.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void bucket_items(int64_t bucket, const int32_t* row_ptr, int nblk,
                                              int64_t q_start, int64_t Nq, int chunk,
-                                             int32_t& n_loc, int32_t& n_non, int32_t& items) {
+                                             bool with_local, int32_t& n_loc, int32_t& n_non,
+                                             int32_t& items) {
   const int b = (int)(bucket % nblk);
   const int32_t cnt = row_ptr[bucket + 1] - row_ptr[bucket];
   const int64_t lo = max(q_start, (int64_t)b * kBlock);
   const int64_t hi = min(q_start + Nq, (int64_t)(b + 1) * kBlock);
-  n_loc = hi > lo ? (int32_t)(hi - lo) : 0;
+  n_loc = hi > lo && !with_local ? (int32_t)(hi - lo) : 0;
   n_non = cnt - n_loc;
   items = (n_non + chunk - 1) / chunk;
 }
@@ -58,7 +61,7 @@ __device__ __forceinline__ void bucket_items(int64_t bucket, const int32_t* row_
 // the attention kernel's fetch counter, cleared here.
 __global__ __launch_bounds__(1024) void build_items_kernel(const int32_t* __restrict__ row_ptr,
                                                            int64_t nb, int nblk, int64_t q_start,
-                                                           int64_t Nq, int chunk,
+                                                           int64_t Nq, int chunk, bool with_local,
                                                            int4* __restrict__ items,
                                                            int32_t* __restrict__ n_items) {
   __shared__ int32_t full[1024], rest[1024];
@@ -68,7 +71,7 @@ __global__ __launch_bounds__(1024) void build_items_kernel(const int32_t* __rest
   int32_t nf = 0, nr = 0;
   for (int64_t x = lo; x < hi; ++x) {
     int32_t n_loc, n_non, it;
-    bucket_items(x, row_ptr, nblk, q_start, Nq, chunk, n_loc, n_non, it);
+    bucket_items(x, row_ptr, nblk, q_start, Nq, chunk, with_local, n_loc, n_non, it);
     nf += n_non / chunk;
     nr += n_non % chunk != 0;
   }
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(1024) void build_items_kernel(const int32_t* __rest
   int32_t pf = t ? full[t - 1] : 0, pr = n_full + (t ? rest[t - 1] : 0);
   for (int64_t x = lo; x < hi; ++x) {
     int32_t n_loc, n_non, it;
-    bucket_items(x, row_ptr, nblk, q_start, Nq, chunk, n_loc, n_non, it);
+    bucket_items(x, row_ptr, nblk, q_start, Nq, chunk, with_local, n_loc, n_non, it);
     const int32_t start = row_ptr[x] + n_loc;
     int32_t done = 0;
     for (; done + chunk <= n_non; done += chunk)
@@ -116,8 +119,6 @@ __global__ __launch_bounds__(1024) void build_items_kernel(const int32_t* __rest
 // (h+1)*DH/2)), which leaves the dot products unchanged.
 // ---------------------------------------------------------------------------
 constexpr int kVtPitch = kBlock + 4;  // elements per V^T row
-constexpr int kMaxItem = 2048;        // max query positions per work item
-constexpr int kMaxK = 32;             // max selected blocks per (query, group)
 
 template <int DH>
 struct AttnSmem {
@@ -128,17 +129,6 @@ struct AttnSmem {
 };
 
 __device__ __forceinline__ int vt_off(int d, int key) { return d * kVtPitch + key; }
-
-// XOR swizzle of the 16-byte chunks of K row `row` in LDS.  A fragment read
-// has 16 lanes (16 consecutive rows, one chunk index) in flight per LDS
-// cycle; the swizzle sends them to 16 distinct 4-bank groups.  d_h = 128:
-// a row spans all 64 banks, so rows differ in their low 4 bits.  d_h = 64:
-// two rows share a bank row (row & 1 picks the half), so the next 3 bits
-// pick the chunk.
-template <int DH>
-__device__ __forceinline__ int k_swz(int row) {
-  return DH == 128 ? (row & 15) : ((row >> 1) & 7);
-}
 
 // K and V of block (group r, keys key0..key0+127); keys >= Nk read as 0.
 // Every global load is issued before the first LDS store, so the block
@@ -171,7 +161,7 @@ __device__ __forceinline__ void stage_kv(AttnSmem<DH>& sm, const __bf16* __restr
 #pragma unroll
   for (int u = 0; u < KL; ++u) {
     const int id = t + 256 * u, row = id / CH, c = id % CH;
-    *reinterpret_cast<bf16x8*>(&sm.k[row * DH + 8 * (c ^ k_swz<DH>(row))]) = kr[u];
+    *reinterpret_cast<bf16x8*>(&sm.k[row * DH + 8 * (c ^ row_swz<DH>(row))]) = kr[u];
   }
 #pragma unroll
   for (int u = 0; u < VL; ++u) {
@@ -228,7 +218,7 @@ template <int DH>
 __device__ __forceinline__ bf16x8 k_frag(const AttnSmem<DH>& sm, int g, int s, int h, int n) {
   const int krow = 32 * g + n;
   return *reinterpret_cast<const bf16x8*>(
-      &sm.k[krow * DH + 8 * (((DH / 16) * h + s) ^ k_swz<DH>(krow))]);
+      &sm.k[krow * DH + 8 * (((DH / 16) * h + s) ^ row_swz<DH>(krow))]);
 }
 
 // V^T fragment (MFMA A: 32 d x 16 keys) for d = 32*dg + n and the keys of
@@ -600,10 +590,10 @@ int attn_max_chunk() { return kMaxItem; }
 int64_t attn_max_items(int64_t nb, int64_t nnz, int chunk) { return nb + nnz / chunk + 1; }
 
 hipError_t launch_build_items(const int32_t* row_ptr, int64_t nb, int nblk, int64_t q_start,
-                              int64_t Nq, int chunk, int4* items, int32_t* n_items,
-                              hipStream_t stream) {
-  build_items_kernel<<<1, 1024, 0, stream>>>(row_ptr, nb, nblk, q_start, Nq, chunk, items,
-                                             n_items);
+                              int64_t Nq, int chunk, bool with_local, int4* items,
+                              int32_t* n_items, hipStream_t stream) {
+  build_items_kernel<<<1, 1024, 0, stream>>>(row_ptr, nb, nblk, q_start, Nq, chunk, with_local,
+                                             items, n_items);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@
 //   (4) merge of the k partials in ascending block order through their
 //       log-sum-exp.
 #include "common.h"
+#include "lds_rows.h"
 #include "msa_internal.h"
 
 namespace msa {
@@ -88,11 +89,6 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const __bf16* __restri
 // (d pair, head group) accumulates up to four heads per pass, reading each
 // V pair once for all of them.
 template <int DH>
-__device__ __forceinline__ int dk_swz(int row) {
-  return DH == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-
-template <int DH>
 __global__ __launch_bounds__(256) void decode_attn_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ sel, int64_t N, int H_q, int H_kv, int k, float scale_log2,
@@ -132,7 +128,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
 #pragma unroll
     for (int u = 0; u < LD; ++u) {
       const int id = t + 256 * u, row = id / CH, c = id % CH;
-      *reinterpret_cast<bf16x8*>(ks + row * DH + 8 * (c ^ dk_swz<DH>(row))) = kx[u];
+      *reinterpret_cast<bf16x8*>(ks + row * DH + 8 * (c ^ row_swz<DH>(row))) = kx[u];
       *reinterpret_cast<bf16x8*>(vs + row * DH + 8 * c) = vx[u];
     }
   }
@@ -153,7 +149,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(
       for (int j = 0; j < HB; ++j) sc[j] = 0.f;
       for (int c = 0; c < CH; ++c) {
         const bf16x8 kx =
-            *reinterpret_cast<const bf16x8*>(ks + key * DH + 8 * (c ^ dk_swz<DH>(key)));
+            *reinterpret_cast<const bf16x8*>(ks + key * DH + 8 * (c ^ row_swz<DH>(key)));
         float kf[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) kf[u] = bf2f(kx[u]);

@@ -153,7 +153,7 @@ msa_status run_attn(const void* Q, const void* K, const void* V, const int32_t* 
   const int nblk = (int)cdiv(q_start + Nq, kB);
   AttnWs w = attn_layout(ws, q_start, Nq, H_q, H_kv, d_h, k);
   msa_status st = hip_status(msa::launch_build_items(row_ptr, (int64_t)H_kv * nblk, nblk,
-                                                     q_start, Nq, (int)g_opt_chunk, w.items,
+                                                     q_start, Nq, (int)g_opt_chunk, false, w.items,
                                                      w.n_items, s),
                              "work-list launch");
   if (st) return st;
@@ -297,6 +297,64 @@ msa_status msa_sparse_attn_fwd(const void* Q, const void* K, const void* V,
   if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   msa_status st = run_attn(Q, K, V, row_ptr, col, slot, q_start, Nq, Nk, H_q, H_kv, d_h, k,
                            scale, O, lse, ws, static_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+// ---------------------------------------------------------------- index KL
+struct KlWs {
+  int4* items;
+  int32_t* n_items;
+  float* part;   // per (query, group, slot): sum t ln t, sum t s, ln sum exp s
+  double* sums;  // per 4096 (query, group) values, for the deterministic total
+  int64_t max_items;
+  size_t bytes;
+};
+
+KlWs kl_layout(void* ws, int64_t q_start, int64_t Nq, int H_kv, int k) {
+  const int64_t nblk = cdiv(q_start + Nq, kB);
+  const int64_t nnz = nnz_of(q_start, Nq, H_kv, kB, k);
+  KlWs w;
+  Carve c(ws);
+  w.max_items = msa::attn_max_items((int64_t)H_kv * nblk, nnz, (int)g_opt_chunk);
+  w.items = c.take<int4>(sizeof(int4) * (size_t)w.max_items);
+  w.n_items = c.take<int32_t>(2 * sizeof(int32_t));
+  w.part = c.take<float>(sizeof(float) * 3 * (size_t)Nq * H_kv * k);
+  w.sums = c.take<double>(sizeof(double) * (size_t)msa::kl_sum_partials(Nq * H_kv));
+  w.bytes = c.off;
+  return w;
+}
+
+size_t msa_index_kl_workspace_bytes(int64_t q_start, int64_t Nq, int H_kv, int B_k, int k) {
+  if (check_common(q_start, Nq, H_kv, B_k, k)) return 0;
+  return kl_layout(nullptr, q_start, Nq, H_kv, k).bytes;
+}
+
+msa_status msa_index_kl(const void* Q, const void* K, const void* q_idx, const void* k_idx,
+                        const float* lse, const int32_t* row_ptr, const int32_t* col,
+                        const uint8_t* slot, int64_t q_start, int64_t Nq, int64_t Nk, int H_q,
+                        int H_kv, int d_h, int d_idx, int B_k, int k, float scale, float* kl,
+                        double* kl_sum, void* ws, size_t ws_bytes, void* stream) {
+  if (msa_status st = check_common(q_start, Nq, H_kv, B_k, k)) return st;
+  if (msa_status st = check_attn_shapes(H_q, H_kv, d_h)) return st;
+  if (msa_status st = check_index_dims(d_idx)) return st;
+  if (!Q || !K || !q_idx || !k_idx || !lse || !row_ptr || !col || !slot || !kl)
+    return fail(MSA_ERR_INVALID_ARG, "null Q, K, q_idx, k_idx, lse, row_ptr, col, slot or kl");
+  if (Nk < q_start + Nq) return fail(MSA_ERR_INVALID_ARG, "Nk must be >= q_start + Nq");
+  if (!(scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "scale must be > 0");
+  const size_t need = kl_layout(nullptr, q_start, Nq, H_kv, k).bytes;
+  if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  KlWs w = kl_layout(ws, q_start, Nq, H_kv, k);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nblk = (int)cdiv(q_start + Nq, kB);
+  msa_status st = hip_status(msa::launch_build_items(row_ptr, (int64_t)H_kv * nblk, nblk, q_start,
+                                                     Nq, (int)g_opt_chunk, true, w.items,
+                                                     w.n_items, s),
+                             "work-list launch");
+  if (st) return st;
+  st = hip_status(msa::launch_index_kl(Q, K, q_idx, k_idx, lse, col, slot, w.items, w.n_items,
+                                       w.max_items, q_start, Nq, Nk, H_q, H_kv, d_h, d_idx, nblk,
+                                       k, scale, w.part, kl, w.sums, kl_sum, s),
+                  "index KL launch");
   return st ? st : ok();
 }
 

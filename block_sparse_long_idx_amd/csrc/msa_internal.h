@@ -31,8 +31,8 @@ hipError_t launch_invert(const int32_t* sel, int64_t q_start, int64_t Nq, int H_
 int attn_max_chunk();
 int64_t attn_max_items(int64_t nb, int64_t nnz, int chunk);
 hipError_t launch_build_items(const int32_t* row_ptr, int64_t nb, int nblk, int64_t q_start,
-                              int64_t Nq, int chunk, int4* items, int32_t* n_items,
-                              hipStream_t stream);
+                              int64_t Nq, int chunk, bool with_local, int4* items,
+                              int32_t* n_items, hipStream_t stream);
 hipError_t launch_attn(const void* Q, const void* K, const void* V, const int32_t* col,
                        const uint8_t* slot, const int4* items, int32_t* n_items,
                        int64_t max_items, int64_t q_start, int64_t Nq, int64_t Nk, int H_q,
@@ -42,6 +42,15 @@ hipError_t launch_combine(const void* Q, const void* K, const void* V, const voi
                           const float* lse_s, int64_t q_start, int64_t Nq, int64_t Nk, int H_q,
                           int H_kv, int d_h, int k, float scale, float* O, float* lse,
                           hipStream_t stream);
+
+// kl.hip
+int64_t kl_sum_partials(int64_t n);
+hipError_t launch_index_kl(const void* Q, const void* K, const void* q_idx, const void* k_idx,
+                           const float* lse, const int32_t* col, const uint8_t* slot,
+                           const int4* items, int32_t* n_items, int64_t max_items,
+                           int64_t q_start, int64_t Nq, int64_t Nk, int H_q, int H_kv, int d_h,
+                           int d_idx, int nblk, int k, float scale, float* part, float* kl,
+                           double* sums, double* kl_sum, hipStream_t stream);
 
 // decode.hip
 hipError_t launch_decode_scan(const void* q_idx, const void* k_idx, int B, int64_t N, int H_kv,

@@ -57,6 +57,9 @@ def load():
         "msa_decode_workspace_bytes": ([i32, i64, i32, i32, i32, i32, i32], sz),
         "msa_decode": ([P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32, f32, P, P,
                         P, P, sz, P], i32),
+        "msa_index_kl_workspace_bytes": ([i64, i64, i32, i32, i32], sz),
+        "msa_index_kl": ([P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32, i32, i32, i32,
+                          i32, f32, P, P, P, sz, P], i32),
         "msa_set_option": ([i32, i64], i32),
         "msa_get_option": ([i32], i64),
     }
@@ -178,6 +181,36 @@ def sparse_attn_fwd(Q, K, V, row_ptr, col, slot, k, q_start=0, Nq=None, scale=No
                                    scale, _ptr(O), _ptr(lse), _ptr(ws), ws.numel(),
                                    _stream(Q)))
     return O, lse
+
+
+def index_kl_workspace_bytes(q_start, Nq, H_kv, k, B_k=B_K) -> int:
+    return load().msa_index_kl_workspace_bytes(q_start, Nq, H_kv, B_k, k)
+
+
+def index_kl(Q, K, q_idx, k_idx, lse, row_ptr, col, slot, k, q_start=0, Nq=None, scale=None,
+             B_k=B_K, want_sum=True, kl=None, kl_sum=None, ws=None):
+    """Index-alignment KL(teacher || student) per (query, group) for rows
+    [q_start, q_start+Nq): (kl fp32 [Nq, H_kv], kl_sum fp64 [1] or None).
+    `lse` is the Main Branch's [Nq, H_q] output for the same rows."""
+    _need_cuda(Q, K, q_idx, k_idx, lse, row_ptr, col, slot)
+    Nk, H_kv, d_h = K.shape
+    H_q = Q.shape[1]
+    d_idx = k_idx.shape[2]
+    Nq = Q.shape[0] - q_start if Nq is None else Nq
+    scale = 1.0 / math.sqrt(d_h) if scale is None else scale
+    lib = load()
+    dev = Q.device
+    if kl is None:
+        kl = torch.empty((Nq, H_kv), dtype=torch.float32, device=dev)
+    if kl_sum is None and want_sum:
+        kl_sum = torch.empty(1, dtype=torch.float64, device=dev)
+    if ws is None:
+        ws = _workspace(lib.msa_index_kl_workspace_bytes(q_start, Nq, H_kv, B_k, k), dev)
+    _check(lib.msa_index_kl(_ptr(Q), _ptr(K), _ptr(q_idx), _ptr(k_idx), _ptr(lse),
+                            _ptr(row_ptr), _ptr(col), _ptr(slot), q_start, Nq, Nk, H_q, H_kv,
+                            d_h, d_idx, B_k, k, scale, _ptr(kl), _ptr(kl_sum), _ptr(ws),
+                            ws.numel(), _stream(Q)))
+    return kl, kl_sum
 
 
 def prefill_workspace_bytes(N, H_q, H_kv, d_h, d_idx, k, chunk=0, B_k=B_K) -> int:

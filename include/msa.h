@@ -147,6 +147,35 @@ msa_status msa_prefill(const void *Q, const void *K, const void *V,
                        float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Index-alignment KL, forward value (section 03, "KL Loss"; section 05
+ * part 2: the forward keeps the LSE, so the KL needs no softmax pass of its
+ * own).  For query i and group r over the token set T of its selection
+ * (tokens j <= i of the selected blocks):
+ *   teacher t_j = (1/G) sum over the group's heads h of
+ *                 exp(scale * Q[i,h,:].K[j,r,:] - lse[i,h])
+ *   student u_j = softmax over T of q_idx[i,r,:].k_idx[j,r,:]
+ *   kl[i-q_start, r] = sum_{j in T} t_j (ln t_j - ln u_j)
+ * The teacher is normalised by the forward's lse, so pass the lse that
+ * msa_sparse_attn_fwd / msa_prefill wrote for the same Q, K and selection.
+ * Partials are merged per (i, r) in ascending slot order, so the result is
+ * deterministic.
+ *   Q [>= q_start+Nq, H_q, d_h], K [Nk, H_kv, d_h], q_idx, k_idx
+ *     [., H_kv, d_idx]: full-sequence bases, bf16
+ *   lse:     [Nq, H_q] fp32 (natural log), this chunk's rows
+ *   row_ptr, col, slot: msa_invert_index output for the same chunk
+ *   kl:      out [Nq, H_kv] fp32
+ *   kl_sum:  out, nullable: one double, the sum of kl over the chunk
+ *            (fixed-order reduction; divide by the row count for the mean)
+ */
+size_t msa_index_kl_workspace_bytes(int64_t q_start, int64_t Nq, int H_kv, int B_k, int k);
+msa_status msa_index_kl(const void *Q, const void *K, const void *q_idx, const void *k_idx,
+                        const float *lse, const int32_t *row_ptr, const int32_t *col,
+                        const uint8_t *slot, int64_t q_start, int64_t Nq, int64_t Nk,
+                        int H_q, int H_kv, int d_h, int d_idx, int B_k, int k,
+                        float scale, float *kl, double *kl_sum, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/*
  * Decode: one new query per sequence at the last cache row (position N-1,
  * so it sees the whole cache and its local block is the last one).  Same
  * selection and attention as that prefill row, computed Q-outer: the

@@ -57,6 +57,9 @@ def _load():
         lib.oracle_decode_one.argtypes = [P, P, P, P, P, i64, i32, i32, i32,
                                           i32, i32, i32, f64, P, P, P, i32]
         lib.oracle_decode_one.restype = None
+        lib.oracle_index_kl.argtypes = [P, P, P, P, P, P, i64, i32, i32, i32, i32,
+                                        i32, i32, f64, P, i32]
+        lib.oracle_index_kl.restype = None
         _lib = lib
     return _lib
 
@@ -145,6 +148,29 @@ def invert(sel, q_start, nblk):
                                 _ptr(row_ptr), _ptr(col), _ptr(slot))
     assert nnz == cap
     return row_ptr, col[:nnz], slot[:nnz]
+
+
+def index_kl(q_rows, k_idx, Q_rows, K, sel, rows, scale, B_k=128, nthreads=None):
+    """Index-alignment KL(teacher || student) of each (row, group) over the
+    tokens of its selection.
+
+    q_rows: uint16 [nrows, H_kv, d_idx]; k_idx: uint16 [Nk, H_kv, d_idx];
+    Q_rows: uint16 [nrows, H_q, d_h]; K: uint16 [Nk, H_kv, d_h]; sel: int32
+    [nrows, H_kv, k].  Returns fp64 [nrows, H_kv].
+    """
+    q_rows, k_idx, Q_rows, K = _u16(q_rows), _u16(k_idx), _u16(Q_rows), _u16(K)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    nrows, H_kv, d_idx = q_rows.shape
+    H_q, d_h = Q_rows.shape[1], Q_rows.shape[2]
+    k = sel.shape[2]
+    assert sel.shape == (nrows, H_kv, k) and Q_rows.shape[0] == nrows
+    assert K.shape[1] == H_kv and k_idx.shape[1] == H_kv
+    kl = np.empty((nrows, H_kv), dtype=np.float64)
+    _load().oracle_index_kl(_ptr(q_rows), _ptr(k_idx), _ptr(Q_rows), _ptr(K), _ptr(sel),
+                            _ptr(rows), nrows, H_q, H_kv, d_h, d_idx, B_k, k, float(scale),
+                            _ptr(kl), nthreads or threads())
+    return kl
 
 
 def decode_one(q, q_idx, K, V, k_idx, k, scale, B_k=128, nthreads=None):

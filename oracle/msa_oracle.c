@@ -158,6 +158,75 @@ static void attend_one(const uint16_t *q_vec /* [d_h] */, const uint16_t *K,
     *lse = m + log(l);
 }
 
+/*
+ * Index-alignment KL of one (query row, group) over the token set T of
+ * its selection (section 03, "KL Loss": on the visible token set induced by
+ * the selected blocks, the student is the softmax of the index scores and
+ * the teacher is the mean over the group's G query heads of their Main
+ * Branch attention distributions; the indexer minimises KL(teacher ||
+ * student), averaged over positions and groups).
+ *   teacher t_j = (1/G) sum_h softmax_T(scale * Q[i,h,:] . K[j,r,:])_j
+ *   student u_j = softmax_T(q_idx[i,r,:] . k_idx[j,r,:])_j
+ *   KL = sum_{j in T, t_j > 0} t_j (ln t_j - ln u_j)
+ * Every softmax is taken over the whole of T at once, in fp64.
+ */
+static double kl_one(const uint16_t *q_row /* [d_idx] */, const uint16_t *k_idx,
+                     const uint16_t *Q_heads /* [G, d_h] */, const uint16_t *K,
+                     int64_t i, int r, int G, int H_kv, int d_h, int d_idx, int B_k,
+                     const int32_t *sel_row, int k, double scale, double *buf /* 3*k*B_k */)
+{
+    double *tok = buf;                    /* token ids of T, as doubles */
+    double *t = buf + (int64_t)k * B_k;   /* teacher */
+    double *s = t + (int64_t)k * B_k;     /* scores, reused */
+    int64_t n = 0;
+    for (int u = 0; u < k; ++u) {
+        int32_t b = sel_row[u];
+        if (b < 0)
+            continue;
+        for (int64_t j = (int64_t)b * B_k; j < ((int64_t)b + 1) * B_k && j <= i; ++j)
+            tok[n++] = (double)j;
+    }
+    for (int64_t a = 0; a < n; ++a)
+        t[a] = 0.0;
+    for (int g = 0; g < G; ++g) {
+        const uint16_t *qv = Q_heads + (int64_t)g * d_h;
+        double m = -INFINITY;
+        for (int64_t a = 0; a < n; ++a) {
+            int64_t j = (int64_t)tok[a];
+            double dot = 0.0;
+            for (int d = 0; d < d_h; ++d)
+                dot += widen_bf16(qv[d]) * widen_bf16(K[(j * H_kv + r) * d_h + d]);
+            s[a] = dot * scale;
+            if (s[a] > m)
+                m = s[a];
+        }
+        double z = 0.0;
+        for (int64_t a = 0; a < n; ++a)
+            z += exp(s[a] - m);
+        for (int64_t a = 0; a < n; ++a)
+            t[a] += exp(s[a] - m) / z / (double)G;
+    }
+    double m = -INFINITY;
+    for (int64_t a = 0; a < n; ++a) {
+        int64_t j = (int64_t)tok[a];
+        double dot = 0.0;
+        for (int d = 0; d < d_idx; ++d)
+            dot += widen_bf16(q_row[d]) * widen_bf16(k_idx[(j * H_kv + r) * d_idx + d]);
+        s[a] = dot;
+        if (dot > m)
+            m = dot;
+    }
+    double z = 0.0;
+    for (int64_t a = 0; a < n; ++a)
+        z += exp(s[a] - m);
+    double lse = m + log(z);
+    double kl = 0.0;
+    for (int64_t a = 0; a < n; ++a)
+        if (t[a] > 0.0)
+            kl += t[a] * (log(t[a]) - (s[a] - lse));
+    return kl;
+}
+
 /* ------------------------------------------------------------------ */
 /* Threaded drivers over query rows                                   */
 /* ------------------------------------------------------------------ */
@@ -171,7 +240,8 @@ typedef struct {
     double scale;
     int32_t *sel;      /* select: output; attend: input */
     double *O, *lse;
-    int mode;          /* 0 select, 1 attend */
+    double *kl;        /* index KL: output [nrows, H_kv] */
+    int mode;          /* 0 select, 1 attend, 2 index KL */
     /* per thread */
     int tid, nthreads;
 } job_t;
@@ -200,6 +270,20 @@ static void *run_rows(void *arg)
         }
         free(P);
         free(taken);
+    } else if (jb->mode == 2) {
+        int G = jb->H_q / jb->H_kv;
+        double *buf = (double *)malloc(sizeof(double) * 3 * (size_t)jb->k * jb->B_k);
+        for (int64_t u = jb->tid; u < jb->nrows * jb->H_kv; u += jb->nthreads) {
+            int64_t n = u / jb->H_kv;
+            int r = (int)(u % jb->H_kv);
+            int64_t i = jb->rows[n];
+            jb->kl[n * jb->H_kv + r] =
+                kl_one(jb->q_rows + (n * jb->H_kv + r) * jb->d_idx, jb->k_idx,
+                       jb->Q_rows + (n * jb->H_q + (int64_t)r * G) * jb->d_h, jb->K, i, r, G,
+                       jb->H_kv, jb->d_h, jb->d_idx, jb->B_k,
+                       jb->sel + (n * jb->H_kv + r) * jb->k, jb->k, jb->scale, buf);
+        }
+        free(buf);
     } else {
         int G = jb->H_q / jb->H_kv;
         double *s_buf = (double *)malloc(sizeof(double) * (size_t)jb->k * jb->B_k);
@@ -288,6 +372,39 @@ void oracle_attend(const uint16_t *Q_rows, const uint16_t *K, const uint16_t *V,
     jb.O = O;
     jb.lse = lse;
     jb.mode = 1;
+    run_threads(&jb, nthreads);
+}
+
+/*
+ * Index-alignment KL (see kl_one) for a list of query rows, given their
+ * selection.
+ *   q_rows: [nrows, H_kv, d_idx]; k_idx: [Nk, H_kv, d_idx]
+ *   Q_rows: [nrows, H_q, d_h]; K: [Nk, H_kv, d_h]
+ *   kl: out [nrows, H_kv] fp64
+ */
+void oracle_index_kl(const uint16_t *q_rows, const uint16_t *k_idx, const uint16_t *Q_rows,
+                     const uint16_t *K, const int32_t *sel, const int64_t *rows, int64_t nrows,
+                     int H_q, int H_kv, int d_h, int d_idx, int B_k, int k, double scale,
+                     double *kl, int nthreads)
+{
+    job_t jb;
+    memset(&jb, 0, sizeof jb);
+    jb.q_rows = q_rows;
+    jb.k_idx = k_idx;
+    jb.Q_rows = Q_rows;
+    jb.K = K;
+    jb.sel = (int32_t *)sel;
+    jb.rows = rows;
+    jb.nrows = nrows;
+    jb.H_q = H_q;
+    jb.H_kv = H_kv;
+    jb.d_h = d_h;
+    jb.d_idx = d_idx;
+    jb.B_k = B_k;
+    jb.k = k;
+    jb.scale = scale;
+    jb.kl = kl;
+    jb.mode = 2;
     run_threads(&jb, nthreads);
 }
 
