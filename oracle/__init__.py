@@ -60,6 +60,9 @@ def _load():
         lib.oracle_index_kl.argtypes = [P, P, P, P, P, P, i64, i32, i32, i32, i32,
                                         i32, i32, f64, P, i32]
         lib.oracle_index_kl.restype = None
+        lib.oracle_attend_backward.argtypes = [P, P, P, P, P, i64, i32, i32, i32, i32, i32,
+                                               f64, P, P, P, i32]
+        lib.oracle_attend_backward.restype = None
         _lib = lib
     return _lib
 
@@ -171,6 +174,29 @@ def index_kl(q_rows, k_idx, Q_rows, K, sel, rows, scale, B_k=128, nthreads=None)
                             _ptr(rows), nrows, H_q, H_kv, d_h, d_idx, B_k, k, float(scale),
                             _ptr(kl), nthreads or threads())
     return kl
+
+
+def attend_backward(Q, K, V, dO, sel, scale, B_k=128, nthreads=None):
+    """Main Branch gradients for every row 0..N-1 given the output gradient.
+
+    Q, dO: uint16 [N, H_q, d_h]; K, V: uint16 [N, H_kv, d_h]; sel: int32
+    [N, H_kv, k].  Returns (dQ [N, H_q, d_h], dK [N, H_kv, d_h],
+    dV [N, H_kv, d_h]), fp64.
+    """
+    Q, K, V, dO = _u16(Q), _u16(K), _u16(V), _u16(dO)
+    sel = np.ascontiguousarray(sel, dtype=np.int32)
+    N, H_q, d_h = Q.shape
+    H_kv = K.shape[1]
+    k = sel.shape[2]
+    assert dO.shape == Q.shape and K.shape == V.shape == (N, H_kv, d_h)
+    assert sel.shape == (N, H_kv, k)
+    dQ = np.empty((N, H_q, d_h), dtype=np.float64)
+    dK = np.empty((N, H_kv, d_h), dtype=np.float64)
+    dV = np.empty((N, H_kv, d_h), dtype=np.float64)
+    _load().oracle_attend_backward(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(sel), N, H_q,
+                                   H_kv, d_h, B_k, k, float(scale), _ptr(dQ), _ptr(dK),
+                                   _ptr(dV), nthreads or threads())
+    return dQ, dK, dV
 
 
 def decode_one(q, q_idx, K, V, k_idx, k, scale, B_k=128, nthreads=None):

@@ -409,6 +409,135 @@ void oracle_index_kl(const uint16_t *q_rows, const uint16_t *k_idx, const uint16
 }
 
 /*
+ * Main Branch backward over the selected token sets: the gradients of a
+ * scalar loss with output gradient dO, for the forward above (section 02:
+ * Main Branch = exact softmax attention over the selected blocks; the
+ * selection itself is not differentiable -- section 03 -- so no gradient
+ * reaches the Index Branch from this loss).  Per query row i and head h
+ * (group r), over T = the tokens j <= i of the row's selected blocks:
+ *   s_j = scale * Q[i,h].K[j,r],  p = softmax_T(s),  O = sum_j p_j V[j,r]
+ *   dp_j = dO[i,h].V[j,r],  ds_j = p_j (dp_j - dO[i,h].O)
+ *   dQ[i,h]  = scale * sum_j ds_j K[j,r]
+ *   dK[j,r] += scale * ds_j Q[i,h]        dV[j,r] += p_j dO[i,h]
+ * Every softmax is taken over the whole of T at once, in fp64; dK and dV
+ * sum over every (row, head) whose T contains j.
+ *   Q, dO: [N, H_q, d_h] (all rows 0..N-1); K, V: [N, H_kv, d_h]
+ *   sel: [N, H_kv, k]; dQ out [N, H_q, d_h]; dK, dV out [N, H_kv, d_h]
+ */
+typedef struct {
+    const uint16_t *Q, *K, *V, *dO;
+    const int32_t *sel;
+    int64_t N;
+    int H_q, H_kv, d_h, B_k, k;
+    double scale;
+    double *dQ, *dK, *dV;   /* dK, dV: this thread's private accumulators */
+    int tid, nthreads;
+} bwd_job_t;
+
+static void *run_bwd(void *arg)
+{
+    bwd_job_t *jb = (bwd_job_t *)arg;
+    const int G = jb->H_q / jb->H_kv, d_h = jb->d_h, B_k = jb->B_k;
+    const int64_t cap = (int64_t)jb->k * B_k;
+    int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
+    double *p = (double *)malloc(sizeof(double) * (size_t)cap);
+    double *O = (double *)malloc(sizeof(double) * (size_t)d_h);
+    for (int64_t u = jb->tid; u < jb->N * jb->H_q; u += jb->nthreads) {
+        const int64_t i = u / jb->H_q;
+        const int h = (int)(u % jb->H_q), r = h / G;
+        const uint16_t *q = jb->Q + (i * jb->H_q + h) * d_h;
+        const uint16_t *go = jb->dO + (i * jb->H_q + h) * d_h;
+        const int32_t *srow = jb->sel + (i * jb->H_kv + r) * jb->k;
+        int64_t n = 0;
+        for (int t = 0; t < jb->k; ++t) {
+            if (srow[t] < 0)
+                continue;
+            for (int64_t j = (int64_t)srow[t] * B_k; j < ((int64_t)srow[t] + 1) * B_k && j <= i; ++j)
+                tok[n++] = j;
+        }
+        double m = -INFINITY;
+        for (int64_t a = 0; a < n; ++a) {
+            double dot = 0.0;
+            for (int d = 0; d < d_h; ++d)
+                dot += widen_bf16(q[d]) * widen_bf16(jb->K[(tok[a] * jb->H_kv + r) * d_h + d]);
+            p[a] = dot * jb->scale;
+            if (p[a] > m)
+                m = p[a];
+        }
+        double z = 0.0;
+        for (int64_t a = 0; a < n; ++a) {
+            p[a] = exp(p[a] - m);
+            z += p[a];
+        }
+        for (int d = 0; d < d_h; ++d)
+            O[d] = 0.0;
+        for (int64_t a = 0; a < n; ++a) {
+            p[a] /= z;
+            for (int d = 0; d < d_h; ++d)
+                O[d] += p[a] * widen_bf16(jb->V[(tok[a] * jb->H_kv + r) * d_h + d]);
+        }
+        double Dv = 0.0;
+        for (int d = 0; d < d_h; ++d)
+            Dv += widen_bf16(go[d]) * O[d];
+        double *dq = jb->dQ + (i * jb->H_q + h) * d_h;
+        for (int d = 0; d < d_h; ++d)
+            dq[d] = 0.0;
+        for (int64_t a = 0; a < n; ++a) {
+            const int64_t base = (tok[a] * jb->H_kv + r) * d_h;
+            double dp = 0.0;
+            for (int d = 0; d < d_h; ++d)
+                dp += widen_bf16(go[d]) * widen_bf16(jb->V[base + d]);
+            const double ds = p[a] * (dp - Dv);
+            for (int d = 0; d < d_h; ++d) {
+                dq[d] += jb->scale * ds * widen_bf16(jb->K[base + d]);
+                jb->dK[base + d] += jb->scale * ds * widen_bf16(q[d]);
+                jb->dV[base + d] += p[a] * widen_bf16(go[d]);
+            }
+        }
+    }
+    free(tok);
+    free(p);
+    free(O);
+    return NULL;
+}
+
+void oracle_attend_backward(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                            const uint16_t *dO, const int32_t *sel, int64_t N, int H_q,
+                            int H_kv, int d_h, int B_k, int k, double scale, double *dQ,
+                            double *dK, double *dV, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    const size_t kv = (size_t)N * H_kv * d_h;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    bwd_job_t *jobs = (bwd_job_t *)malloc(sizeof(bwd_job_t) * (size_t)nthreads);
+    for (int t = 0; t < nthreads; ++t) {
+        bwd_job_t *jb = &jobs[t];
+        jb->Q = Q; jb->K = K; jb->V = V; jb->dO = dO; jb->sel = sel;
+        jb->N = N; jb->H_q = H_q; jb->H_kv = H_kv; jb->d_h = d_h; jb->B_k = B_k; jb->k = k;
+        jb->scale = scale; jb->dQ = dQ;
+        jb->dK = (double *)calloc(kv, sizeof(double));
+        jb->dV = (double *)calloc(kv, sizeof(double));
+        jb->tid = t;
+        jb->nthreads = nthreads;
+        pthread_create(&th[t], NULL, run_bwd, jb);
+    }
+    for (size_t e = 0; e < kv; ++e)
+        dK[e] = dV[e] = 0.0;
+    for (int t = 0; t < nthreads; ++t) {
+        pthread_join(th[t], NULL);
+        for (size_t e = 0; e < kv; ++e) {
+            dK[e] += jobs[t].dK[e];
+            dV[e] += jobs[t].dV[e];
+        }
+        free(jobs[t].dK);
+        free(jobs[t].dV);
+    }
+    free(th);
+    free(jobs);
+}
+
+/*
  * Inverted index: the selection table turned around, from "which blocks
  * does each query read" to "which queries hit each block" (section 05,
  * part 2: KV-outer execution gathers, per KV block, the queries that
