@@ -300,6 +300,70 @@ msa_status msa_sparse_attn_fwd(const void* Q, const void* K, const void* V,
   return st ? st : ok();
 }
 
+// ---------------------------------------------------------------- backward
+struct BwdWs {
+  int4* items;
+  int32_t* n_items;
+  int4* units;
+  int32_t* n_units;
+  float* D;       // dO . O per (row, head)
+  void* dq_part;  // bf16 dQ partials [Nq*k + 1][H_kv][d_h/4][G][4]
+  int64_t max_items;
+  size_t bytes;
+};
+
+BwdWs bwd_layout(void* ws, int64_t q_start, int64_t Nq, int H_q, int H_kv, int d_h, int k) {
+  const int64_t nblk = cdiv(q_start + Nq, kB);
+  const int64_t nnz = nnz_of(q_start, Nq, H_kv, kB, k);
+  BwdWs w;
+  Carve c(ws);
+  w.max_items = msa::attn_max_items((int64_t)H_kv * nblk, nnz, (int)g_opt_chunk);
+  w.items = c.take<int4>(sizeof(int4) * (size_t)w.max_items);
+  w.n_items = c.take<int32_t>(2 * sizeof(int32_t));
+  w.units = c.take<int4>(sizeof(int4) * (size_t)msa::bwd_max_units((int64_t)H_kv * nblk));
+  w.n_units = c.take<int32_t>(2 * sizeof(int32_t));
+  w.D = c.take<float>(sizeof(float) * (size_t)Nq * H_q);
+  w.dq_part = c.take<void>(2 * ((size_t)Nq * k + 1) * H_q * d_h);
+  w.bytes = c.off;
+  return w;
+}
+
+size_t msa_sparse_attn_bwd_workspace_bytes(int64_t q_start, int64_t Nq, int H_q, int H_kv,
+                                           int d_h, int B_k, int k) {
+  if (check_common(q_start, Nq, H_kv, B_k, k) || check_attn_shapes(H_q, H_kv, d_h)) return 0;
+  return bwd_layout(nullptr, q_start, Nq, H_q, H_kv, d_h, k).bytes;
+}
+
+msa_status msa_sparse_attn_bwd(const void* Q, const void* K, const void* V, const float* O,
+                               const float* lse, const void* dO, const int32_t* row_ptr,
+                               const int32_t* col, const uint8_t* slot, int64_t q_start,
+                               int64_t Nq, int64_t Nk, int H_q, int H_kv, int d_h, int B_k,
+                               int k, float scale, float* dQ, float* dK, float* dV, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (msa_status st = check_common(q_start, Nq, H_kv, B_k, k)) return st;
+  if (msa_status st = check_attn_shapes(H_q, H_kv, d_h)) return st;
+  if (!Q || !K || !V || !O || !lse || !dO || !row_ptr || !col || !slot || !dQ || !dK || !dV)
+    return fail(MSA_ERR_INVALID_ARG, "null Q, K, V, O, lse, dO, row_ptr, col, slot, dQ, dK or dV");
+  if (Nk < q_start + Nq) return fail(MSA_ERR_INVALID_ARG, "Nk must be >= q_start + Nq");
+  if (!(scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "scale must be > 0");
+  const size_t need = bwd_layout(nullptr, q_start, Nq, H_q, H_kv, d_h, k).bytes;
+  if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  BwdWs w = bwd_layout(ws, q_start, Nq, H_q, H_kv, d_h, k);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nblk = (int)cdiv(q_start + Nq, kB);
+  msa_status st = hip_status(msa::launch_build_items(row_ptr, (int64_t)H_kv * nblk, nblk, q_start,
+                                                     Nq, (int)g_opt_chunk, true, w.items,
+                                                     w.n_items, s),
+                             "work-list launch");
+  if (st) return st;
+  st = hip_status(msa::launch_attn_bwd(Q, K, V, O, lse, dO, row_ptr, col, slot, w.items,
+                                       w.n_items, w.max_items, w.units, w.n_units, q_start, Nq,
+                                       Nk, H_q, H_kv, d_h, nblk, k, scale, w.D, w.dq_part, dQ, dK,
+                                       dV, s),
+                  "backward launch");
+  return st ? st : ok();
+}
+
 // ---------------------------------------------------------------- index KL
 struct KlWs {
   int4* items;

@@ -43,6 +43,16 @@ hipError_t launch_combine(const void* Q, const void* K, const void* V, const voi
                           int H_kv, int d_h, int k, float scale, float* O, float* lse,
                           hipStream_t stream);
 
+// attn_bwd.hip
+int64_t bwd_max_units(int64_t nb);
+hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const float* O,
+                           const float* lse, const void* dO, const int32_t* row_ptr,
+                           const int32_t* col, const uint8_t* slot, const int4* items,
+                           int32_t* n_items, int64_t max_items, int4* units, int32_t* n_units,
+                           int64_t q_start, int64_t Nq, int64_t Nk, int H_q, int H_kv, int d_h,
+                           int nblk, int k, float scale, float* Dbuf, void* dq_part, float* dQ,
+                           float* dK, float* dV, hipStream_t stream);
+
 // kl.hip
 int64_t kl_sum_partials(int64_t n);
 hipError_t launch_index_kl(const void* Q, const void* K, const void* q_idx, const void* k_idx,

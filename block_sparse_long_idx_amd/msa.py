@@ -60,6 +60,9 @@ def load():
         "msa_index_kl_workspace_bytes": ([i64, i64, i32, i32, i32], sz),
         "msa_index_kl": ([P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32, i32, i32, i32,
                           i32, f32, P, P, P, sz, P], i32),
+        "msa_sparse_attn_bwd_workspace_bytes": ([i64, i64, i32, i32, i32, i32, i32], sz),
+        "msa_sparse_attn_bwd": ([P, P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32, i32,
+                                 i32, i32, f32, P, P, P, P, sz, P], i32),
         "msa_set_option": ([i32, i64], i32),
         "msa_get_option": ([i32], i64),
     }
@@ -181,6 +184,33 @@ def sparse_attn_fwd(Q, K, V, row_ptr, col, slot, k, q_start=0, Nq=None, scale=No
                                    scale, _ptr(O), _ptr(lse), _ptr(ws), ws.numel(),
                                    _stream(Q)))
     return O, lse
+
+
+def sparse_attn_bwd(Q, K, V, O, lse, dO, row_ptr, col, slot, k, q_start=0, Nq=None,
+                    scale=None, B_k=B_K, dQ=None, dK=None, dV=None, ws=None):
+    """Main Branch backward for rows [q_start, q_start+Nq): returns (dQ, dK, dV).
+    dK and dV are added to (fresh zero tensors when not given)."""
+    _need_cuda(Q, K, V, O, lse, dO, row_ptr, col, slot)
+    Nk, H_kv, d_h = K.shape
+    H_q = Q.shape[1]
+    Nq = Q.shape[0] - q_start if Nq is None else Nq
+    scale = 1.0 / math.sqrt(d_h) if scale is None else scale
+    lib = load()
+    dev = Q.device
+    if dQ is None:
+        dQ = torch.empty((Nq, H_q, d_h), dtype=torch.float32, device=dev)
+    if dK is None:
+        dK = torch.zeros((Nk, H_kv, d_h), dtype=torch.float32, device=dev)
+    if dV is None:
+        dV = torch.zeros((Nk, H_kv, d_h), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(lib.msa_sparse_attn_bwd_workspace_bytes(q_start, Nq, H_q, H_kv, d_h,
+                                                                B_k, k), dev)
+    _check(lib.msa_sparse_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse), _ptr(dO),
+                                   _ptr(row_ptr), _ptr(col), _ptr(slot), q_start, Nq, Nk, H_q,
+                                   H_kv, d_h, B_k, k, scale, _ptr(dQ), _ptr(dK), _ptr(dV),
+                                   _ptr(ws), ws.numel(), _stream(Q)))
+    return dQ, dK, dV
 
 
 def index_kl_workspace_bytes(q_start, Nq, H_kv, k, B_k=B_K) -> int:

@@ -147,6 +147,38 @@ msa_status msa_prefill(const void *Q, const void *K, const void *V,
                        float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Main Branch backward (section 02: exact softmax attention over the
+ * selected blocks, so its gradients are those of softmax attention on each
+ * row's token set; section 03: the selection is not differentiable, so no
+ * gradient reaches the Index Branch from this loss).  For query positions
+ * i in [q_start, q_start+Nq), head h (group r), T = the tokens j <= i of the
+ * row's selected blocks, p = the forward's probabilities (rebuilt from lse),
+ * D = dO[i,h].O[i,h]:
+ *   ds_j = p_j (dO[i,h].V[j,r] - D)
+ *   dQ[i,h]  = scale * sum_j ds_j K[j,r]
+ *   dK[j,r] += scale * ds_j Q[i,h]      dV[j,r] += p_j dO[i,h]
+ * dQ rows are written; dK and dV are ADDED to (zero them before the first
+ * chunk), so calling this chunk by chunk over a sequence accumulates the
+ * whole sequence's gradients.  Per-(i, h, block) dQ partials are bf16 and
+ * summed in ascending slot order; each key's dK/dV sums are formed in one
+ * work-group: the result is deterministic.
+ *   Q [., H_q, d_h], K, V [Nk, H_kv, d_h]: bf16 full-sequence bases
+ *   O [Nq, H_q, d_h] fp32, lse [Nq, H_q] fp32: this chunk's forward outputs
+ *   dO [Nq, H_q, d_h] bf16
+ *   row_ptr, col, slot: msa_invert_index output for the same chunk
+ *   dQ out [Nq, H_q, d_h] fp32; dK, dV in/out [Nk, H_kv, d_h] fp32
+ */
+size_t msa_sparse_attn_bwd_workspace_bytes(int64_t q_start, int64_t Nq, int H_q,
+                                           int H_kv, int d_h, int B_k, int k);
+msa_status msa_sparse_attn_bwd(const void *Q, const void *K, const void *V,
+                               const float *O, const float *lse, const void *dO,
+                               const int32_t *row_ptr, const int32_t *col,
+                               const uint8_t *slot, int64_t q_start, int64_t Nq,
+                               int64_t Nk, int H_q, int H_kv, int d_h, int B_k, int k,
+                               float scale, float *dQ, float *dK, float *dV, void *ws,
+                               size_t ws_bytes, void *stream);
+
+/*
  * Index-alignment KL, forward value (section 03, "KL Loss"; section 05
  * part 2: the forward keeps the LSE, so the KL needs no softmax pass of its
  * own).  For query i and group r over the token set T of its selection
