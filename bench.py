@@ -10,7 +10,7 @@ Prints one JSON line: prefill tokens/s (value), effective TFLOP/s by the
 MSA FLOP formula 4*H_q*d_h*N*k*B_k + H_kv*d_idx*N^2 (as a fraction of the
 2.5 PFLOP/s bf16 MFMA peak), per-stage times, the roofline of the dominant
 kernel, the CPU oracle timed on sampled rows, and the index-alignment KL
-pass, 128K-prefill and 32 x 1M decode figures.
+pass, Main Branch backward, 128K-prefill and 32 x 1M decode figures.
 """
 import argparse
 import json
@@ -190,6 +190,65 @@ def time_kl(pf, cfg, t, reps=2):
             "bytes_per_step": nbytes}
 
 
+def time_bwd(pf, cfg, t, reps=2):
+    """The Main Branch backward (msa_sparse_attn_bwd) over every chunk of a
+    step, from the step's O and lse and a seeded output gradient.  Each
+    chunk's inverted index is rebuilt first (its buffers are shared between
+    chunks); only the backward calls are timed."""
+    import torch
+    from block_sparse_long_idx_amd.synth import make_grad_output
+    msa = pf.msa
+    lib = msa.load()
+    dev = t["Q"].device
+    dO = make_grad_output(cfg.N, cfg.H_q, cfg.d_h, seed=cfg.seed + 17, device=dev)
+    ws = max(lib.msa_sparse_attn_bwd_workspace_bytes(q0, nq, cfg.H_q, cfg.H_kv, cfg.d_h,
+                                                     cfg.B_k, cfg.k) for q0, nq in pf.chunks)
+    ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+    dQ = torch.empty((cfg.N, cfg.H_q, cfg.d_h), dtype=torch.float32, device=dev)
+    dK = torch.empty((cfg.N, cfg.H_kv, cfg.d_h), dtype=torch.float32, device=dev)
+    dV = torch.empty_like(dK)
+    total_ms, nnz = 0.0, 0
+    for rep in range(reps + 1):
+        dK.zero_()
+        dV.zero_()
+        ms = 0.0
+        for q0, nq in pf.chunks:
+            rp, col, slot = msa.invert_index(pf.sel[q0:q0 + nq], q_start=q0, ws=pf.ws_v,
+                                             row_ptr=pf.row_ptr, col=pf.col, slot=pf.slot)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            msa.sparse_attn_bwd(t["Q"], t["K"], t["V"], pf.O[q0:q0 + nq], pf.lse[q0:q0 + nq],
+                                dO[q0:q0 + nq], rp, col, slot, cfg.k, q_start=q0, Nq=nq,
+                                scale=cfg.scale, dQ=dQ[q0:q0 + nq], dK=dK, dV=dV, ws=ws)
+            b.record()
+            b.synchronize()
+            ms += a.elapsed_time(b)
+            if rep == 0:
+                nnz += msa.selection_nnz(q0, nq, cfg.H_kv, cfg.k)
+        if rep > 0:
+            total_ms += ms
+    ms = total_ms / reps
+    G = cfg.H_q // cfg.H_kv
+    d = cfg.d_h
+    # per (query, head, selected block): the dQ pass reads Q, dO, lse, delta
+    # and writes a bf16 dQ partial; the dK/dV pass reads Q, dO, lse, delta
+    # again; the reduce reads the partial back.  Per (query, head): delta
+    # reads O (fp32) and dO, the reduce writes dQ (fp32).
+    pairs = nnz * G
+    nbytes = pairs * (12 * d + 16) + cfg.N * cfg.H_q * (6 * d + 4 * d + 4)
+    flops = 10.0 * cfg.H_q * d * cfg.N * cfg.k * cfg.B_k
+    ok = bool(torch.isfinite(dQ).all().item() and torch.isfinite(dK).all().item()
+              and torch.isfinite(dV).all().item())
+    del dO, ws
+    return {"ms_per_step": round(ms, 3),
+            "effective_tflops": round(flops / (ms / 1e3) / 1e12, 2),
+            "frac_bf16_peak": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "formula_tflop_per_step": round(flops / 1e12, 3),
+            "GB_per_s": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_per_step": nbytes, "finite": ok}
+
+
 def cpu_baseline(cfg, t, n_rows):
     """The oracle, as it stands, on n_rows query rows spread over the sequence."""
     import numpy as np
@@ -337,14 +396,16 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on {args.cpu_rows} sampled rows")
         out["cpu_baseline"] = cpu_baseline(cfg, t, args.cpu_rows)
-    kl_leg = None
+    kl_leg = bwd_leg = None
     if not args.no_extra:
         log("[bench] index KL leg")
         kl_leg = time_kl(pf, cfg, t)
+        log("[bench] Main Branch backward leg")
+        bwd_leg = time_bwd(pf, cfg, t)
     del pf, t
     torch.cuda.empty_cache()
     if not args.no_extra:
-        extra = {f"index_kl_{cfg.name}": kl_leg}
+        extra = {f"index_kl_{cfg.name}": kl_leg, f"attn_bwd_{cfg.name}": bwd_leg}
         if cfg.name != "128k":
             c2 = CONFIGS["128k"]
             log("[bench] 128K prefill leg")

@@ -8,18 +8,19 @@
 // (recomputed from the saved lse), D = dO . O:
 //   dp_j = dO . V_j,  ds_j = p_j (dp_j - D)
 //   dQ = scale * sum_j ds_j K_j,  dK_j += scale * ds_j Q,  dV_j += p_j dO
-// Both passes run KV-outer on the forward's inverted index (local positions
-// included, with the causal mask), like the forward:
-//   dQ:    work items of <= chunk positions of one bucket; 32-row tiles
-//          (rows = (position, head) pairs) on the lanes: S^T = K Q^T,
-//          dP^T = V dO^T, dS in registers, dQ^T = K^T dS^T; a bf16 partial
-//          per (i, h, slot), summed per (i, h) in ascending slot order.
-//   dK/dV: one work-group per non-empty bucket, its four waves owning 32
-//          keys each and sweeping all the bucket's rows in 32-row tiles with
-//          keys on the lanes: S = Q K^T, dP = dO V^T, then dV += P^T dO and
-//          dK += dS^T Q contract over the rows.  Each key's sums are complete
-//          inside one work-group, so they are added to dK/dV once, with no
-//          partial buffers and no atomics.
+// One KV-outer pass over the forward's inverted index (local positions
+// included, with the causal mask).  A work unit is one bucket (group r,
+// block b), or a fixed-size slice of a large one.  Its work-group keeps the
+// block's K and V in registers (each of the four waves owns 32 keys) and
+// sweeps the unit's rows -- (position, head) pairs -- in 32-row tiles that
+// are double-buffered in LDS, row-major for S = Q K^T and dP = dO V^T and
+// transposed for dV += P^T dO and dK += dS^T Q (the contractions over
+// rows).  Each tile's dS goes through LDS so that the waves, now owning 32
+// d each, form dQ^T = K^T dS^T over all 128 keys; that is stored as a bf16
+// partial per (i, h, slot) and summed per (i, h) in ascending slot order by
+// a second kernel.  A whole bucket adds its dK/dV sums to the outputs at
+// the end; the slices of a split bucket write fp32 partials that a third
+// kernel sums in slice order.  Deterministic, no atomics on the outputs.
 #include "common.h"
 #include "lds_rows.h"
 #include "msa_internal.h"
@@ -31,21 +32,23 @@ namespace msa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kTp = kBlock + 4;  // pitch of a transposed [d][128 keys] block
-constexpr int kRp = 32 + 4;      // pitch of a transposed [d][32 rows] tile
+constexpr int kRp = 32 + 4;       // pitch of a transposed [d][32 rows] tile
+constexpr int kDsp = kBlock + 4;  // pitch of the [32 rows][128 keys] dS tile
+constexpr int kUnitRows = 16384;  // rows per work unit, at most
+constexpr int kUnitPos = 1024;    // positions per work unit, at most
 
 // A fragment (MFMA A or B: 32 rows x 16 d at k-step s) of a row-major
-// swizzled block; lane half h covers d in [h*D/2, (h+1)*D/2).
+// swizzled tile; lane half h covers d in [h*D/2, (h+1)*D/2).
 template <int D>
 __device__ __forceinline__ bf16x8 rm_frag(const __bf16* blk, int row, int s, int h) {
   return *reinterpret_cast<const bf16x8*>(
       &blk[row * D + 8 * (((D / 16) * h + s) ^ row_swz<D>(row))]);
 }
 
-// Fragment with the contraction over 16 "rows" of a transposed block
-// t[d][pitch]: lane half h takes rows c0 + 4h + {0..3} and c0 + 8 + 4h +
-// {0..3}, which is the order in which an accumulator's entries 8u..8u+7
-// hold rows 16u.. (so an accumulator can be the other operand).
+// Fragment with the contraction over 16 entries c0.. of a row of t[.][PITCH]:
+// lane half h takes entries c0 + 4h + {0..3} and c0 + 8 + 4h + {0..3}, which
+// is the order in which an accumulator's registers 8u..8u+7 hold rows 16u..
+// (so an accumulator can be the other operand).
 template <int PITCH>
 __device__ __forceinline__ bf16x8 tr_frag(const __bf16* t, int d, int c0, int h) {
   const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&t[d * PITCH + c0 + 4 * h]);
@@ -53,34 +56,9 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16* t, int d, int c0, int h)
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// K, V of block (r, key0..): row-major swizzled; rows >= Nk read as 0.
-template <int DH>
-__device__ __forceinline__ void stage_rm2(__bf16* kd, __bf16* vd, const __bf16* __restrict__ K,
-                                          const __bf16* __restrict__ V, int r, int H_kv,
-                                          int64_t key0, int64_t Nk, int t, int nthreads) {
-  constexpr int CH = DH / 8;
-  for (int id0 = 0; id0 < kBlock * CH; id0 += 4 * nthreads) {
-    bf16x8 kr[4], vr[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int id = id0 + t + nthreads * u, row = id / CH, c = id % CH;
-      const bool in = id < kBlock * CH && key0 + row < Nk;
-      const int64_t off = ((key0 + row) * H_kv + r) * DH + 8 * c;
-      kr[u] = in ? *reinterpret_cast<const bf16x8*>(K + off) : bf16x8{};
-      vr[u] = in ? *reinterpret_cast<const bf16x8*>(V + off) : bf16x8{};
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int id = id0 + t + nthreads * u, row = id / CH, c = id % CH;
-      if (id < kBlock * CH) {
-        *reinterpret_cast<bf16x8*>(&kd[row * DH + 8 * (c ^ row_swz<DH>(row))]) = kr[u];
-        *reinterpret_cast<bf16x8*>(&vd[row * DH + 8 * (c ^ row_swz<DH>(row))]) = vr[u];
-      }
-    }
-  }
-}
-
 }  // namespace
+
+int bwd_unit_positions(int G) { return std::min(kUnitPos, std::max(1, kUnitRows / G)); }
 
 // ---------------------------------------------------------------------------
 // D = dO . O per (row, head): 16 lanes per row, one 8-wide chunk each.
@@ -107,129 +85,321 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const __bf16* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// dQ pass.
-template <int DH>
-struct BwdQSmem {
-  __bf16 k[kBlock * DH];   // row-major, swizzled
-  __bf16 v[kBlock * DH];   // row-major, swizzled
-  __bf16 kt[DH * kTp];     // K transposed, padded
-  int32_t pos[kMaxItem];
-  uint8_t sl[kMaxItem];
-};
+// Work units: every non-empty bucket, split into slices of at most `upos`
+// positions when larger.  Units of split buckets and buckets of at least
+// upos/2 entries come first.  A split bucket also gets a record (bucket,
+// first partial, slices) for the dK/dV partial sum.
+__global__ __launch_bounds__(1024) void build_bwd_units_kernel(
+    const int32_t* __restrict__ row_ptr, int64_t nb, int upos, int4* __restrict__ units,
+    int32_t* __restrict__ n_units, int4* __restrict__ splits, int32_t* __restrict__ n_splits) {
+  __shared__ int4 sc[1024];
+  const int t = threadIdx.x;
+  const int64_t per = ceil_div(nb, (int64_t)1024);
+  const int64_t lo = min(nb, per * t), hi = min(nb, per * (t + 1));
+  int4 c = make_int4(0, 0, 0, 0);  // large units, small units, split buckets, slices
+  for (int64_t x = lo; x < hi; ++x) {
+    const int32_t cnt = row_ptr[x + 1] - row_ptr[x];
+    const int32_t nu = (cnt + upos - 1) / upos;
+    if (nu > 1) {
+      c.x += nu;
+      c.z += 1;
+      c.w += nu;
+    } else if (2 * cnt >= upos) {
+      c.x += 1;
+    } else if (cnt > 0) {
+      c.y += 1;
+    }
+  }
+  sc[t] = c;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int4 v = t >= o ? sc[t - o] : make_int4(0, 0, 0, 0);
+    __syncthreads();
+    const int4 m = sc[t];
+    sc[t] = make_int4(m.x + v.x, m.y + v.y, m.z + v.z, m.w + v.w);
+    __syncthreads();
+  }
+  const int4 tot = sc[1023];
+  const int4 ex = t ? sc[t - 1] : make_int4(0, 0, 0, 0);
+  int32_t ub = ex.x, us = tot.x + ex.y, sp = ex.z, pi = ex.w;
+  for (int64_t x = lo; x < hi; ++x) {
+    const int32_t s0 = row_ptr[x], cnt = row_ptr[x + 1] - s0;
+    const int32_t nu = (cnt + upos - 1) / upos;
+    if (nu > 1) {
+      splits[sp++] = make_int4((int)x, pi, nu, 0);
+      for (int32_t s = 0; s < nu; ++s)
+        units[ub++] = make_int4((int)x, s0 + s * upos, min(upos, cnt - s * upos), pi + s);
+      pi += nu;
+    } else if (2 * cnt >= upos) {
+      units[ub++] = make_int4((int)x, s0, cnt, -1);
+    } else if (cnt > 0) {
+      units[us++] = make_int4((int)x, s0, cnt, -1);
+    }
+  }
+  if (t == 1023) {
+    n_units[0] = tot.x + tot.y;
+    n_units[1] = 0;
+    n_splits[0] = tot.z;
+  }
+}
 
 template <int DH>
-__global__ __launch_bounds__(512) void bwd_dq_kernel(
+struct BwdSmem {
+  __bf16 qr[2][32 * DH];    // the tile's Q rows, row-major swizzled
+  __bf16 gr[2][32 * DH];    // the tile's dO rows
+  __bf16 qt[2][DH * kRp];   // the same, transposed [d][row]
+  __bf16 gt[2][DH * kRp];
+  __bf16 ds[2][32 * kDsp];  // dS [row][key]
+  int32_t lim[2][32];       // per tile row: last visible key of the block (-1: none)
+  float l2[2][32];          // lse * log2(e)
+  float dv[2][32];          // D = dO . O
+  int32_t pos[kUnitPos];    // the unit's query positions
+  uint8_t sl[kUnitPos];     // and the block's slot in each one's selection
+};
+
+// One work-group per CU (its LDS), so the register budget is one wave per
+// SIMD: the scheduler may spend it on keeping LDS reads ahead of the MFMAs.
+template <int DH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_fused_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ D,
     const int32_t* __restrict__ col, const uint8_t* __restrict__ slot,
-    const int4* __restrict__ items, int32_t* __restrict__ n_items, int64_t q_start, int64_t Nk,
-    int H_q, int H_kv, int G, float inv_G, int nblk, int k, int64_t spare, float scale_log2,
-    __bf16* __restrict__ part) {
-  constexpr int S = DH / 16, NDG = DH / 32, NW = 8;
+    const int4* __restrict__ units, int32_t* __restrict__ n_units, int64_t q_start, int64_t Nk,
+    int H_q, int H_kv, int G, float inv_G, int nblk, int k, int64_t spare, float scale,
+    float scale_log2, __bf16* __restrict__ part, float* __restrict__ kvpart,
+    float* __restrict__ dK, float* __restrict__ dV) {
+  constexpr int S = DH / 16, NDG = DH / 32, CH = DH / 8;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  BwdQSmem<DH>& sm = *reinterpret_cast<BwdQSmem<DH>*>(smem_raw);
+  BwdSmem<DH>& sm = *reinterpret_cast<BwdSmem<DH>*>(smem_raw);
   __shared__ int32_t next;
   const int t = threadIdx.x, wave = t >> 6;
-  const int32_t total = n_items[0];
+  const int32_t total = n_units[0];
   for (;;) {
-    if (t == 0) next = atomicAdd(&n_items[1], 1);
+    if (t == 0) next = atomicAdd(&n_units[1], 1);
     __syncthreads();
-    const int32_t item_id = next;
-    if (item_id >= total) return;
-    const int4 it = items[item_id];
-    const int bucket = it.x, start = it.y, count = it.z;
+    const int32_t unit_id = next;
+    if (unit_id >= total) return;
+    const int4 un = units[unit_id];
+    const int bucket = un.x, start = un.y, count = un.z, pidx = un.w;
     const int r = bucket / nblk, b = bucket % nblk;
-    int tl = t;  // per-item addresses are rebuilt, not hoisted and spilled
+    int tl = t;  // per-unit addresses are rebuilt, not hoisted and spilled
     asm volatile("" : "+v"(tl));
-    for (int p = tl; p < count; p += 64 * NW) {
-      sm.pos[p] = col[start + p];
-      sm.sl[p] = slot[start + p];
-    }
-    stage_rm2<DH>(sm.k, sm.v, K, V, r, H_kv, (int64_t)b * kBlock, Nk, tl, 64 * NW);
-    __syncthreads();
-    // K^T from the staged rows: each thread moves 4 keys x 8 d
-    for (int id = tl; id < (kBlock / 4) * (DH / 8); id += 64 * NW) {
-      const int kq = id % (kBlock / 4), c = id / (kBlock / 4);
-      bf16x8 rw[4];
+    {
+      // count <= kUnitPos = 4 * 256: all loads first, then the LDS stores
+      int32_t pv[kUnitPos / 256];
+      uint8_t sv[kUnitPos / 256];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = 4 * kq + u;
-        rw[u] = *reinterpret_cast<const bf16x8*>(&sm.k[row * DH + 8 * (c ^ row_swz<DH>(row))]);
+      for (int u = 0; u < kUnitPos / 256; ++u) {
+        const int p = tl + 256 * u;
+        pv[u] = col[start + min(p, count - 1)];
+        sv[u] = slot[start + min(p, count - 1)];
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<bf16x4*>(&sm.kt[(8 * c + e) * kTp + 4 * kq]) =
-            bf16x4{rw[0][e], rw[1][e], rw[2][e], rw[3][e]};
+      for (int u = 0; u < kUnitPos / 256; ++u) {
+        const int p = tl + 256 * u;
+        if (p < count) {
+          sm.pos[p] = pv[u];
+          sm.sl[p] = sv[u];
+        }
+      }
     }
-    __syncthreads();
-
     const int lane = tl & 63, h = lane >> 5, n = lane & 31;
-    const int nrows = count * G;
-    const int ntile = (nrows + 31) / 32;
-    for (int tile = wave; tile < ntile; tile += NW) {
-      const int R = tile * 32 + n;
-      const bool ok = R < nrows;
-      const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
-      const int pos = sm.pos[pp];
-      const int hq = r * G + (ok ? R - pp * G : 0);
-      const int64_t iq = pos - q_start;
-      const int lim = ok ? pos - b * kBlock : -1;  // visible keys 0..lim
-      bf16x8 qb[S], gb[S];
-      const __bf16* qrow = Q + ((int64_t)pos * H_q + hq) * DH + (DH / 2) * h;
-      const __bf16* grow = dO + (iq * H_q + hq) * DH + (DH / 2) * h;
+    const int kw = 32 * wave;  // this wave's keys kw .. kw+31; its d-slice for dQ
+    const int64_t key0 = (int64_t)b * kBlock;
+    // the wave's keys as the B operand of S and dP (d split by lane half)
+    bf16x8 kf[S], vf[S];
+    {
+      const int64_t key = key0 + kw + n;
+      const bool in = key < Nk;
+      const int64_t off = ((in ? key : key0) * H_kv + r) * DH + (DH / 2) * h;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        qb[s] = *reinterpret_cast<const bf16x8*>(qrow + 8 * s);
-        gb[s] = *reinterpret_cast<const bf16x8*>(grow + 8 * s);
+        kf[s] = *reinterpret_cast<const bf16x8*>(K + off + 8 * s);
+        vf[s] = *reinterpret_cast<const bf16x8*>(V + off + 8 * s);
       }
-      const float l2 = lse[iq * H_q + hq] * kLog2e;
-      const float Dv = D[iq * H_q + hq];
-      // per key group: S^T -> P, dP^T -> dS, packed as the next MFMA's B
-      // operand (keys on the accumulator rows, the row on the lane).  The
-      // LDS index goes through an opaque copy of n so the fragment reads are
-      // not hoisted out of the tile loop into registers.
-      int nn = n;
-      asm volatile("" : "+v"(nn));
-      bf16x8 dsb[4][2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x16 sa = {}, pa = {};
+      for (int s = 0; s < S; ++s) {
+        kf[s] = in ? kf[s] : bf16x8{};
+        vf[s] = in ? vf[s] : bf16x8{};
+      }
+    }
+    // K^T of the wave's d-slice over all 128 keys, as the A operand of dQ^T
+    bf16x8 kT[8];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-          sa = mfma32(rm_frag<DH>(sm.k, 32 * g + nn, s, h), qb[s], sa);
-          pa = mfma32(rm_frag<DH>(sm.v, 32 * g + nn, s, h), gb[s], pa);
+    for (int u = 0; u < 8; ++u) kT[u] = bf16x8{};
+    if (kw < DH) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int64_t key = key0 + 16 * u + (e < 4 ? 4 * h + e : 8 + 4 * h + (e - 4));
+          const __bf16 x = K[((key < Nk ? key : key0) * H_kv + r) * DH + kw + n];
+          kT[u][e] = key < Nk ? x : f2bf(0.f);
+        }
+    }
+    // every fragment load of the unit has landed before the tile loop, so no
+    // wait inside the loop has to cover them
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // tile staging: thread -> (tensor, 4-row group, 16-byte chunk)
+    const int which = tl / (8 * CH);  // 0: Q, 1: dO, 2+: none (wave-uniform)
+    const int it = tl % (8 * CH), rq = it / CH, c = it % CH;
+    const int nrows = count * G;
+    const int ntile = (nrows + 31) / 32;
+    const int hq0 = r * G;
+    bf16x8 x[4];
+    int vmask = 0, mlim = -1;
+    float ml2 = 0.f, mdv = 0.f;
+    auto load = [&](int T) {
+      vmask = 0;
+      if (which < 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int R = 32 * T + 4 * rq + u;
+          const bool ok = R < nrows;
+          const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
+          const int64_t pos = sm.pos[pp];
+          const int hq = hq0 + (ok ? R - pp * G : 0);
+          const __bf16* src = which == 0 ? Q + (pos * H_q + hq) * DH
+                                         : dO + ((pos - q_start) * H_q + hq) * DH;
+          x[u] = *reinterpret_cast<const bf16x8*>(src + 8 * c);
+          vmask |= (int)ok << u;
+        }
+      }
+      if (tl < 32) {
+        const int R = 32 * T + tl;
+        const bool ok = R < nrows;
+        const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
+        const int64_t pos = sm.pos[pp];
+        const int hq = hq0 + (ok ? R - pp * G : 0);
+        const int64_t ih = (pos - q_start) * H_q + hq;
+        ml2 = lse[ih];
+        mdv = D[ih];
+        mlim = ok ? (int)(pos - key0) : -1;
+      }
+    };
+    auto store = [&](int bi) {
+      if (which < 2) {
+        __bf16* rm = which == 0 ? sm.qr[bi] : sm.gr[bi];
+        __bf16* tr = which == 0 ? sm.qt[bi] : sm.gt[bi];
+        bf16x8 y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) y[u] = (vmask >> u) & 1 ? x[u] : bf16x8{};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int row = 4 * rq + u;
+          *reinterpret_cast<bf16x8*>(&rm[row * DH + 8 * (c ^ row_swz<DH>(row))]) = y[u];
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int j = 8 * u + e;
-            const float p = 32 * g + acc_row(j, h) <= lim
-                                ? __builtin_amdgcn_exp2f(sa[j] * scale_log2 - l2)
-                                : 0.f;
-            dsb[g][u][e] = f2bf(p * (pa[j] - Dv));
-          }
+        for (int e = 0; e < 8; ++e)
+          *reinterpret_cast<bf16x4*>(&tr[(8 * c + e) * kRp + 4 * rq]) =
+              bf16x4{y[0][e], y[1][e], y[2][e], y[3][e]};
       }
-      // dQ^T = K^T dS^T, stored as a bf16 partial (rows past the end: spare slot)
-      const int64_t ps = ok ? iq * k + sm.sl[pp] : spare;
-      __bf16* dst = part + (ps * H_kv + r) * (DH / 4) * G * 4 + (hq - r * G + h * G) * 4;
+      if (tl < 32) {
+        sm.lim[bi][tl] = mlim;
+        sm.l2[bi][tl] = ml2 * kLog2e;
+        sm.dv[bi][tl] = mdv;
+      }
+    };
+
+    __syncthreads();  // positions staged
+    load(0);
+    store(0);
+    if (ntile > 1) load(1);
+    __syncthreads();
+    f32x16 ak[NDG], av[NDG];
 #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg) {
+    for (int dg = 0; dg < NDG; ++dg) ak[dg] = av[dg] = f32x16{};
+    for (int T = 0; T < ntile; ++T) {
+      const int bi = T & 1;
+      // LDS indices go through an opaque copy of n so that the fragment
+      // reads stay inside the loop rather than being hoisted into registers
+      int nn = n;
+      asm volatile("" : "+v"(nn));
+      // S = Q K^T and dP = dO V^T for the wave's 32 keys (key on the lane)
+      f32x16 sa = {}, pa = {};
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        sa = mfma32(rm_frag<DH>(sm.qr[bi], nn, s, h), kf[s], sa);
+        pa = mfma32(rm_frag<DH>(sm.gr[bi], nn, s, h), vf[s], pa);
+      }
+      bf16x8 pA[2], dA[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int row = acc_row(8 * u + e, h);
+          const int lm = sm.lim[bi][row];
+          const float l2 = sm.l2[bi][row], dv = sm.dv[bi][row];
+          const float ex = __builtin_amdgcn_exp2f(sa[8 * u + e] * scale_log2 - l2);
+          const float p = kw + n <= lm ? ex : 0.f;
+          pA[u][e] = f2bf(p);
+          dA[u][e] = f2bf(p * (pa[8 * u + e] - dv));
+        }
+      // dV += P^T dO and dK += dS^T Q, contracting over the tile's rows
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          av[dg] = mfma32(pA[u], tr_frag<kRp>(sm.gt[bi], 32 * dg + nn, 16 * u, h), av[dg]);
+          ak[dg] = mfma32(dA[u], tr_frag<kRp>(sm.qt[bi], 32 * dg + nn, 16 * u, h), ak[dg]);
+        }
+      // the wave's dS columns into the shared [row][key] tile
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sm.ds[bi][acc_row(8 * u + e, h) * kDsp + kw + nn] = dA[u][e];
+      // the next tile's rows into the other buffer, then fetch the one after
+      if (T + 1 < ntile) {
+        store(bi ^ 1);
+        if (T + 2 < ntile) load(T + 2);
+      }
+      __syncthreads();
+      // dQ^T for the wave's d-slice = K^T dS^T over the block's 128 keys
+      if (kw < DH) {
         f32x16 acc = {};
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            acc = mfma32(tr_frag<kTp>(sm.kt, 32 * dg + nn, 32 * g + 16 * u, h), dsb[g][u], acc);
-        // d = 32dg + 8qd + 4h + e  ->  d-quad 8dg + 2qd + h
+        for (int u = 0; u < 8; ++u)
+          acc = mfma32(kT[u], tr_frag<kDsp>(sm.ds[bi], nn, 16 * u, h), acc);
+        const int R = 32 * T + n;
+        const bool ok = R < nrows;
+        const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
+        const int64_t ps = ok ? (sm.pos[pp] - q_start) * k + sm.sl[pp] : spare;
+        const int hl = ok ? R - pp * G : 0;
+        __bf16* dst = part + (ps * H_kv + r) * (DH / 4) * G * 4 + hl * 4;
+        // accumulator rows are d = kw + 8qd + 4h + {0..3}: d-quad 8*wave + 2qd + h
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<bf16x4*>(dst + (8 * dg + 2 * qd) * G * 4) =
+          *reinterpret_cast<bf16x4*>(dst + (int64_t)(8 * wave + 2 * qd + h) * G * 4) =
               bf16x4{f2bf(acc[4 * qd]), f2bf(acc[4 * qd + 1]), f2bf(acc[4 * qd + 2]),
                      f2bf(acc[4 * qd + 3])};
       }
     }
-    __syncthreads();  // LDS and `next` are reused by the next item
+    // the unit's dK/dV sums: accumulator rows are keys, the lane is d
+    if (pidx < 0) {
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int64_t key = key0 + kw + acc_row(j, h);
+          if (key < Nk) {
+            const int64_t off = (key * H_kv + r) * DH + 32 * dg + n;
+            dK[off] += scale * ak[dg][j];
+            dV[off] += av[dg][j];
+          }
+        }
+    } else {
+      float* pk = kvpart + (int64_t)pidx * 2 * kBlock * DH;
+#pragma unroll
+      for (int dg = 0; dg < NDG; ++dg)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kr = kw + acc_row(j, h);
+          pk[kr * DH + 32 * dg + n] = ak[dg][j];
+          pk[(kBlock + kr) * DH + 32 * dg + n] = av[dg][j];
+        }
+    }
   }
 }
 
@@ -261,172 +431,42 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const __bf16* __rest
       f32x4{acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale};
 }
 
-// ---------------------------------------------------------------------------
-// dK/dV pass: units = non-empty buckets, the largest first.
-__global__ __launch_bounds__(1024) void build_units_kernel(const int32_t* __restrict__ row_ptr,
-                                                           int64_t nb, int heavy,
-                                                           int4* __restrict__ units,
-                                                           int32_t* __restrict__ n_units) {
-  __shared__ int32_t big[1024], small[1024];
-  const int t = threadIdx.x;
-  const int64_t per = ceil_div(nb, 1024);
-  const int64_t lo = min(nb, per * t), hi = min(nb, per * (t + 1));
-  int32_t nbg = 0, nsm = 0;
-  for (int64_t x = lo; x < hi; ++x) {
-    const int32_t cnt = row_ptr[x + 1] - row_ptr[x];
-    nbg += cnt >= heavy;
-    nsm += cnt > 0 && cnt < heavy;
-  }
-  big[t] = nbg;
-  small[t] = nsm;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int32_t vb = t >= o ? big[t - o] : 0, vs = t >= o ? small[t - o] : 0;
-    __syncthreads();
-    big[t] += vb;
-    small[t] += vs;
-    __syncthreads();
-  }
-  const int32_t n_big = big[1023];
-  int32_t pb = t ? big[t - 1] : 0, ps = n_big + (t ? small[t - 1] : 0);
-  for (int64_t x = lo; x < hi; ++x) {
-    const int32_t cnt = row_ptr[x + 1] - row_ptr[x];
-    if (cnt >= heavy)
-      units[pb++] = make_int4((int)x, row_ptr[x], cnt, 0);
-    else if (cnt > 0)
-      units[ps++] = make_int4((int)x, row_ptr[x], cnt, 0);
-  }
-  if (t == 1023) {
-    n_units[0] = n_big + small[1023];
-    n_units[1] = 0;
-  }
-}
-
+// dK/dV of split buckets: the slices' partials summed in slice order.
 template <int DH>
-struct BwdKvSmem {
-  __bf16 k[kBlock * DH];  // row-major, swizzled
-  __bf16 v[kBlock * DH];
-  __bf16 qr[32 * DH];     // the tile's Q rows, row-major swizzled
-  __bf16 gr[32 * DH];     // the tile's dO rows
-  __bf16 qt[DH * kRp];    // the same, transposed
-  __bf16 gt[DH * kRp];
-  int32_t lim[32];        // per tile row: last visible key of the block
-  float l2[32];           // lse * log2(e)
-  float dv[32];           // D = dO . O
-};
-
-template <int DH>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ D,
-    const int32_t* __restrict__ col, const int4* __restrict__ units,
-    int32_t* __restrict__ n_units, int64_t q_start, int64_t Nk, int H_q, int H_kv, int G,
-    float inv_G, int nblk, float scale, float scale_log2, float* __restrict__ dK,
-    float* __restrict__ dV) {
-  constexpr int S = DH / 16, NDG = DH / 32, CH = DH / 8;
-  extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-  BwdKvSmem<DH>& sm = *reinterpret_cast<BwdKvSmem<DH>*>(smem_raw);
-  __shared__ int32_t next;
-  const int t = threadIdx.x, wave = t >> 6;
-  const int32_t total = n_units[0];
-  for (;;) {
-    if (t == 0) next = atomicAdd(&n_units[1], 1);
-    __syncthreads();
-    const int32_t unit_id = next;
-    if (unit_id >= total) return;
-    const int4 un = units[unit_id];
-    const int bucket = un.x, start = un.y, count = un.z;
-    const int r = bucket / nblk, b = bucket % nblk;
-    int tl = t;
-    asm volatile("" : "+v"(tl));
-    stage_rm2<DH>(sm.k, sm.v, K, V, r, H_kv, (int64_t)b * kBlock, Nk, tl, 256);
-    const int lane = tl & 63, h = lane >> 5, n = lane & 31;
-    const int kw = 32 * wave;  // this wave's keys kw .. kw+31
-    f32x16 ak[NDG], av[NDG];
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(
+    const int4* __restrict__ splits, const int32_t* __restrict__ n_splits,
+    const float* __restrict__ kvpart, int H_kv, int nblk, int64_t Nk, float scale,
+    float* __restrict__ dK, float* __restrict__ dV) {
+  const int32_t ns = n_splits[0];
+  for (int32_t si = blockIdx.x; si < ns; si += gridDim.x) {
+    const int4 sp = splits[si];
+    const int r = sp.x / nblk, b = sp.x % nblk;
+    for (int e = 4 * (int)threadIdx.x; e < kBlock * DH; e += 4 * 256) {
+      f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < sp.z; ++s) {
+        const float* pk = kvpart + (int64_t)(sp.y + s) * 2 * kBlock * DH;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(pk + e);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(pk + kBlock * DH + e);
 #pragma unroll
-    for (int dg = 0; dg < NDG; ++dg) ak[dg] = av[dg] = f32x16{};
-    const int nrows = count * G;
-    for (int R0 = 0; R0 < nrows; R0 += 32) {
-      __syncthreads();  // previous tile's LDS reads are done (and K/V staged)
-      // stage the tile's 32 rows of Q and dO, both layouts
-      for (int id = tl; id < 32 * CH * 2; id += 256) {
-        const int which = id / (32 * CH), rc = id % (32 * CH), rr = rc / CH, c = rc % CH;
-        const int R = R0 + rr;
-        bf16x8 x = {};
-        if (R < nrows) {
-          const int pp = (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G);
-          const int pos = col[start + pp];
-          const int hq = r * G + (R - pp * G);
-          x = which == 0
-                  ? *reinterpret_cast<const bf16x8*>(Q + ((int64_t)pos * H_q + hq) * DH + 8 * c)
-                  : *reinterpret_cast<const bf16x8*>(dO + ((pos - q_start) * H_q + hq) * DH +
-                                                     8 * c);
+        for (int q = 0; q < 4; ++q) {
+          sk[q] += a[q];
+          sv[q] += v[q];
         }
-        __bf16* rmj = which == 0 ? sm.qr : sm.gr;
-        __bf16* trj = which == 0 ? sm.qt : sm.gt;
-        *reinterpret_cast<bf16x8*>(&rmj[rr * DH + 8 * (c ^ row_swz<DH>(rr))]) = x;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) trj[(8 * c + e) * kRp + rr] = x[e];
       }
-      if (tl < 32) {
-        const int R = R0 + tl;
-        int lm = -1;
-        float l = 0.f, dd = 0.f;
-        if (R < nrows) {
-          const int pp = (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G);
-          const int pos = col[start + pp];
-          const int hq = r * G + (R - pp * G);
-          const int64_t iq = pos - q_start;
-          lm = pos - b * kBlock;
-          l = lse[iq * H_q + hq] * kLog2e;
-          dd = D[iq * H_q + hq];
+      const int64_t key = (int64_t)b * kBlock + e / DH;
+      if (key < Nk) {
+        const int64_t off = (key * H_kv + r) * DH + e % DH;
+        f32x4 ok = *reinterpret_cast<const f32x4*>(dK + off);
+        f32x4 ov = *reinterpret_cast<const f32x4*>(dV + off);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          ok[q] += scale * sk[q];
+          ov[q] += sv[q];
         }
-        sm.lim[tl] = lm;
-        sm.l2[tl] = l;
-        sm.dv[tl] = dd;
+        *reinterpret_cast<f32x4*>(dK + off) = ok;
+        *reinterpret_cast<f32x4*>(dV + off) = ov;
       }
-      __syncthreads();
-      // S = Q K^T and dP = dO V^T for the wave's 32 keys (key on the lane)
-      f32x16 sa = {}, pa = {};
-#pragma unroll
-      for (int s = 0; s < S; ++s) {
-        sa = mfma32(rm_frag<DH>(sm.qr, n, s, h), rm_frag<DH>(sm.k, kw + n, s, h), sa);
-        pa = mfma32(rm_frag<DH>(sm.gr, n, s, h), rm_frag<DH>(sm.v, kw + n, s, h), pa);
-      }
-      bf16x8 pA[2], dA[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int row = acc_row(8 * u + e, h);
-          const float p = kw + n <= sm.lim[row]
-                              ? __builtin_amdgcn_exp2f(sa[8 * u + e] * scale_log2 - sm.l2[row])
-                              : 0.f;
-          pA[u][e] = f2bf(p);
-          dA[u][e] = f2bf(p * (pa[8 * u + e] - sm.dv[row]));
-        }
-      // dV += P^T dO and dK += dS^T Q, contracting over the tile's rows
-#pragma unroll
-      for (int dg = 0; dg < NDG; ++dg)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          av[dg] = mfma32(pA[u], tr_frag<kRp>(sm.gt, 32 * dg + n, 16 * u, h), av[dg]);
-          ak[dg] = mfma32(dA[u], tr_frag<kRp>(sm.qt, 32 * dg + n, 16 * u, h), ak[dg]);
-        }
     }
-    // add the bucket's sums: accumulator rows are keys, the lane is d
-#pragma unroll
-    for (int dg = 0; dg < NDG; ++dg)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t key = (int64_t)b * kBlock + kw + acc_row(j, h);
-        if (key < Nk) {
-          const int64_t off = (key * H_kv + r) * DH + 32 * dg + n;
-          dK[off] += scale * ak[dg][j];
-          dV[off] += av[dg][j];
-        }
-      }
-    __syncthreads();  // `next` is reused
   }
 }
 
@@ -441,23 +481,29 @@ static hipError_t bwd_allow(Kern* kern, size_t bytes) {
 
 static hipError_t bwd_prepare() {
   if (bwd_lds_ready) return hipSuccess;
-  hipError_t e = bwd_allow(&bwd_dq_kernel<128>, sizeof(BwdQSmem<128>));
-  if (e == hipSuccess) e = bwd_allow(&bwd_dq_kernel<64>, sizeof(BwdQSmem<64>));
-  if (e == hipSuccess) e = bwd_allow(&bwd_dkdv_kernel<128>, sizeof(BwdKvSmem<128>));
-  if (e == hipSuccess) e = bwd_allow(&bwd_dkdv_kernel<64>, sizeof(BwdKvSmem<64>));
+  hipError_t e = bwd_allow(&bwd_fused_kernel<128>, sizeof(BwdSmem<128>));
+  if (e == hipSuccess) e = bwd_allow(&bwd_fused_kernel<64>, sizeof(BwdSmem<64>));
   if (e == hipSuccess) bwd_lds_ready = true;
   return e;
 }
 
-int64_t bwd_max_units(int64_t nb) { return nb + 1; }
+BwdBounds bwd_bounds(int64_t nb, int64_t nnz, int G) {
+  const int64_t upos = bwd_unit_positions(G);
+  BwdBounds w;
+  w.max_units = nb + nnz / upos + 1;
+  w.max_splits = nnz / (upos + 1) + 1;
+  w.max_slices = 2 * (nnz / upos) + 1;
+  return w;
+}
 
 hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const float* O,
                            const float* lse, const void* dO, const int32_t* row_ptr,
-                           const int32_t* col, const uint8_t* slot, const int4* items,
-                           int32_t* n_items, int64_t max_items, int4* units, int32_t* n_units,
-                           int64_t q_start, int64_t Nq, int64_t Nk, int H_q, int H_kv, int d_h,
-                           int nblk, int k, float scale, float* Dbuf, void* dq_part, float* dQ,
-                           float* dK, float* dV, hipStream_t stream) {
+                           const int32_t* col, const uint8_t* slot, int4* units,
+                           int32_t* n_units, int4* splits, int32_t* n_splits,
+                           const BwdBounds& bounds, int64_t q_start, int64_t Nq, int64_t Nk,
+                           int H_q, int H_kv, int d_h, int nblk, int k, float scale,
+                           float* Dbuf, void* dq_part, float* kvpart, float* dQ, float* dK,
+                           float* dV, hipStream_t stream) {
   hipError_t e = bwd_prepare();
   if (e != hipSuccess) return e;
   const int G = H_q / H_kv;
@@ -475,33 +521,32 @@ hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const fl
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t spare = Nq * k;
   const int nb = H_kv * nblk;
-  dim3 qgrid((unsigned)std::min<int64_t>(max_items, device_cus()));
-  dim3 rgrid((unsigned)ceil_div(rows * (d_h / 4), (int64_t)256));
-  build_units_kernel<<<1, 1024, 0, stream>>>(row_ptr, nb, 1024, units, n_units);
+  build_bwd_units_kernel<<<1, 1024, 0, stream>>>(row_ptr, nb, bwd_unit_positions(G), units,
+                                                 n_units, splits, n_splits);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  dim3 kvgrid((unsigned)std::min<int64_t>(bwd_max_units(nb), device_cus()));
+  dim3 grid((unsigned)std::min<int64_t>(bounds.max_units, device_cus()));
+  dim3 rgrid((unsigned)ceil_div(rows * (d_h / 4), (int64_t)256));
+  dim3 sgrid((unsigned)std::min<int64_t>(bounds.max_splits, 2 * device_cus()));
   if (d_h == 128) {
-    bwd_dq_kernel<128><<<qgrid, 512, sizeof(BwdQSmem<128>), stream>>>(
-        q, kk, v, g, lse, Dbuf, col, slot, items, n_items, q_start, Nk, H_q, H_kv, G, inv_G,
-        nblk, k, spare, scale_log2, part);
+    bwd_fused_kernel<128><<<grid, 256, sizeof(BwdSmem<128>), stream>>>(
+        q, kk, v, g, lse, Dbuf, col, slot, units, n_units, q_start, Nk, H_q, H_kv, G, inv_G,
+        nblk, k, spare, scale, scale_log2, part, kvpart, dK, dV);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     bwd_dq_reduce_kernel<128><<<rgrid, 256, 0, stream>>>(part, q_start, Nq, H_q, H_kv, k,
                                                          scale, dQ);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    bwd_dkdv_kernel<128><<<kvgrid, 256, sizeof(BwdKvSmem<128>), stream>>>(
-        q, kk, v, g, lse, Dbuf, col, units, n_units, q_start, Nk, H_q, H_kv, G, inv_G, nblk,
-        scale, scale_log2, dK, dV);
+    bwd_kv_reduce_kernel<128><<<sgrid, 256, 0, stream>>>(splits, n_splits, kvpart, H_kv, nblk,
+                                                         Nk, scale, dK, dV);
   } else if (d_h == 64) {
-    bwd_dq_kernel<64><<<qgrid, 512, sizeof(BwdQSmem<64>), stream>>>(
-        q, kk, v, g, lse, Dbuf, col, slot, items, n_items, q_start, Nk, H_q, H_kv, G, inv_G,
-        nblk, k, spare, scale_log2, part);
+    bwd_fused_kernel<64><<<grid, 256, sizeof(BwdSmem<64>), stream>>>(
+        q, kk, v, g, lse, Dbuf, col, slot, units, n_units, q_start, Nk, H_q, H_kv, G, inv_G,
+        nblk, k, spare, scale, scale_log2, part, kvpart, dK, dV);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     bwd_dq_reduce_kernel<64><<<rgrid, 256, 0, stream>>>(part, q_start, Nq, H_q, H_kv, k, scale,
                                                         dQ);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    bwd_dkdv_kernel<64><<<kvgrid, 256, sizeof(BwdKvSmem<64>), stream>>>(
-        q, kk, v, g, lse, Dbuf, col, units, n_units, q_start, Nk, H_q, H_kv, G, inv_G, nblk,
-        scale, scale_log2, dK, dV);
+    bwd_kv_reduce_kernel<64><<<sgrid, 256, 0, stream>>>(splits, n_splits, kvpart, H_kv, nblk,
+                                                        Nk, scale, dK, dV);
   } else {
     return hipErrorInvalidValue;
   }

@@ -302,13 +302,14 @@ msa_status msa_sparse_attn_fwd(const void* Q, const void* K, const void* V,
 
 // ---------------------------------------------------------------- backward
 struct BwdWs {
-  int4* items;
-  int32_t* n_items;
   int4* units;
   int32_t* n_units;
+  int4* splits;
+  int32_t* n_splits;
   float* D;       // dO . O per (row, head)
   void* dq_part;  // bf16 dQ partials [Nq*k + 1][H_kv][d_h/4][G][4]
-  int64_t max_items;
+  float* kvpart;  // fp32 dK/dV partials of split buckets [slice][2][B_k][d_h]
+  msa::BwdBounds bounds;
   size_t bytes;
 };
 
@@ -317,13 +318,14 @@ BwdWs bwd_layout(void* ws, int64_t q_start, int64_t Nq, int H_q, int H_kv, int d
   const int64_t nnz = nnz_of(q_start, Nq, H_kv, kB, k);
   BwdWs w;
   Carve c(ws);
-  w.max_items = msa::attn_max_items((int64_t)H_kv * nblk, nnz, (int)g_opt_chunk);
-  w.items = c.take<int4>(sizeof(int4) * (size_t)w.max_items);
-  w.n_items = c.take<int32_t>(2 * sizeof(int32_t));
-  w.units = c.take<int4>(sizeof(int4) * (size_t)msa::bwd_max_units((int64_t)H_kv * nblk));
+  w.bounds = msa::bwd_bounds((int64_t)H_kv * nblk, nnz, H_q / H_kv);
+  w.units = c.take<int4>(sizeof(int4) * (size_t)w.bounds.max_units);
   w.n_units = c.take<int32_t>(2 * sizeof(int32_t));
+  w.splits = c.take<int4>(sizeof(int4) * (size_t)w.bounds.max_splits);
+  w.n_splits = c.take<int32_t>(sizeof(int32_t));
   w.D = c.take<float>(sizeof(float) * (size_t)Nq * H_q);
   w.dq_part = c.take<void>(2 * ((size_t)Nq * k + 1) * H_q * d_h);
+  w.kvpart = c.take<float>(sizeof(float) * 2 * kB * (size_t)d_h * w.bounds.max_slices);
   w.bytes = c.off;
   return w;
 }
@@ -351,16 +353,11 @@ msa_status msa_sparse_attn_bwd(const void* Q, const void* K, const void* V, cons
   BwdWs w = bwd_layout(ws, q_start, Nq, H_q, H_kv, d_h, k);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nblk = (int)cdiv(q_start + Nq, kB);
-  msa_status st = hip_status(msa::launch_build_items(row_ptr, (int64_t)H_kv * nblk, nblk, q_start,
-                                                     Nq, (int)g_opt_chunk, true, w.items,
-                                                     w.n_items, s),
-                             "work-list launch");
-  if (st) return st;
-  st = hip_status(msa::launch_attn_bwd(Q, K, V, O, lse, dO, row_ptr, col, slot, w.items,
-                                       w.n_items, w.max_items, w.units, w.n_units, q_start, Nq,
-                                       Nk, H_q, H_kv, d_h, nblk, k, scale, w.D, w.dq_part, dQ, dK,
-                                       dV, s),
-                  "backward launch");
+  msa_status st = hip_status(
+      msa::launch_attn_bwd(Q, K, V, O, lse, dO, row_ptr, col, slot, w.units, w.n_units,
+                           w.splits, w.n_splits, w.bounds, q_start, Nq, Nk, H_q, H_kv, d_h, nblk,
+                           k, scale, w.D, w.dq_part, w.kvpart, dQ, dK, dV, s),
+      "backward launch");
   return st ? st : ok();
 }
 

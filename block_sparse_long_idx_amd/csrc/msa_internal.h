@@ -44,14 +44,21 @@ hipError_t launch_combine(const void* Q, const void* K, const void* V, const voi
                           hipStream_t stream);
 
 // attn_bwd.hip
-int64_t bwd_max_units(int64_t nb);
+struct BwdBounds {
+  int64_t max_units;   // work units (bucket slices)
+  int64_t max_splits;  // buckets split over several units
+  int64_t max_slices;  // fp32 dK/dV partials of split buckets
+};
+int bwd_unit_positions(int G);
+BwdBounds bwd_bounds(int64_t nb, int64_t nnz, int G);
 hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const float* O,
                            const float* lse, const void* dO, const int32_t* row_ptr,
-                           const int32_t* col, const uint8_t* slot, const int4* items,
-                           int32_t* n_items, int64_t max_items, int4* units, int32_t* n_units,
-                           int64_t q_start, int64_t Nq, int64_t Nk, int H_q, int H_kv, int d_h,
-                           int nblk, int k, float scale, float* Dbuf, void* dq_part, float* dQ,
-                           float* dK, float* dV, hipStream_t stream);
+                           const int32_t* col, const uint8_t* slot, int4* units,
+                           int32_t* n_units, int4* splits, int32_t* n_splits,
+                           const BwdBounds& bounds, int64_t q_start, int64_t Nq, int64_t Nk,
+                           int H_q, int H_kv, int d_h, int nblk, int k, float scale,
+                           float* Dbuf, void* dq_part, float* kvpart, float* dQ, float* dK,
+                           float* dV, hipStream_t stream);
 
 // kl.hip
 int64_t kl_sum_partials(int64_t n);

@@ -106,6 +106,13 @@ def make_prefill_inputs(N, H_q, H_kv, d_h, d_idx, *, n_hot=0, seed=0,
     return dict(Q=Q, K=K, V=V, q_idx=q_idx, k_idx=k_idx)
 
 
+def make_grad_output(N, H_q, d_h, *, seed=0, device="cpu"):
+    """A seeded standard-normal bf16 output gradient dO [N, H_q, d_h]."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return _randn_bf16((N, H_q, d_h), gen, device)
+
+
 def make_decode_inputs(B, N, H_q, H_kv, d_h, d_idx, *, seed=0, device="cpu",
                        seqs=None):
     """Decode inputs for a batch of B sequences, each with an N-token cache.

@@ -161,7 +161,9 @@ msa_status msa_prefill(const void *Q, const void *K, const void *V,
  * chunk), so calling this chunk by chunk over a sequence accumulates the
  * whole sequence's gradients.  Per-(i, h, block) dQ partials are bf16 and
  * summed in ascending slot order; each key's dK/dV sums are formed in one
- * work-group: the result is deterministic.
+ * work-group, or for a block selected by many rows in fixed-size slices
+ * whose fp32 partials are summed in slice order: the result is
+ * deterministic.
  *   Q [., H_q, d_h], K, V [Nk, H_kv, d_h]: bf16 full-sequence bases
  *   O [Nq, H_q, d_h] fp32, lse [Nq, H_q] fp32: this chunk's forward outputs
  *   dO [Nq, H_q, d_h] bf16
