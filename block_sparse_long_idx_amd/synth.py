@@ -113,6 +113,21 @@ def make_grad_output(N, H_q, d_h, *, seed=0, device="cpu"):
     return _randn_bf16((N, H_q, d_h), gen, device)
 
 
+def make_frontend_inputs(N, d_model, H_kv, d_idx, *, seed=0, device="cpu"):
+    """Hidden states and synthetic index-projection weights:
+    hidden [N, d_model] bf16 ~ N(0, 1); Wq, Wk [H_kv*d_idx, d_model] bf16
+    ~ N(0, 1/d_model); gq, gk [d_idx] fp32 ~ 1 + 0.1 N(0, 1)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    hidden = _randn_bf16((N, d_model), gen, device)
+    s = d_model ** -0.5
+    Wq = (torch.randn((H_kv * d_idx, d_model), generator=gen, device=device) * s).to(torch.bfloat16)
+    Wk = (torch.randn((H_kv * d_idx, d_model), generator=gen, device=device) * s).to(torch.bfloat16)
+    gq = 1.0 + 0.1 * torch.randn((d_idx,), generator=gen, device=device)
+    gk = 1.0 + 0.1 * torch.randn((d_idx,), generator=gen, device=device)
+    return dict(hidden=hidden, Wq=Wq, Wk=Wk, gq=gq, gk=gk)
+
+
 def make_decode_inputs(B, N, H_q, H_kv, d_h, d_idx, *, seed=0, device="cpu",
                        seqs=None):
     """Decode inputs for a batch of B sequences, each with an N-token cache.

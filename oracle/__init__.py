@@ -14,6 +14,8 @@ softmax attention over the selected blocks (section 02).
 """
 from __future__ import annotations
 
+from .frontend import index_frontend  # noqa: F401  (fp64 numpy, see frontend.py)
+
 import ctypes
 import os
 import subprocess
