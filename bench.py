@@ -10,7 +10,8 @@ Prints one JSON line: prefill tokens/s (value), effective TFLOP/s by the
 MSA FLOP formula 4*H_q*d_h*N*k*B_k + H_kv*d_idx*N^2 (as a fraction of the
 2.5 PFLOP/s bf16 MFMA peak), per-stage times, the roofline of the dominant
 kernel, the CPU oracle timed on sampled rows, and the index-alignment KL
-pass, Main Branch backward, 128K-prefill and 32 x 1M decode figures.
+pass, Main Branch backward, index front-end, 128K-prefill and 32 x 1M
+decode figures.
 """
 import argparse
 import json
@@ -249,6 +250,40 @@ def time_bwd(pf, cfg, t, reps=2):
             "bytes_per_step": nbytes, "finite": ok}
 
 
+def time_frontend(cfg, reps=3):
+    """The Index Branch front-end (msa_index_frontend: both projections of
+    the hidden states, RMS norm and RoPE) over the whole sequence."""
+    import torch
+    from block_sparse_long_idx_amd import msa
+    from block_sparse_long_idx_amd.synth import make_frontend_inputs
+    t = make_frontend_inputs(cfg.N, cfg.d_model, cfg.H_kv, cfg.d_idx, seed=cfg.seed + 29,
+                             device="cuda")
+    q = torch.empty((cfg.N, cfg.H_kv, cfg.d_idx), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+
+    def run():
+        msa.index_frontend(t["hidden"], t["Wq"], t["Wk"], t["gq"], t["gk"], cfg.H_kv, cfg.d_idx,
+                           q_idx=q, k_idx=k)
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    cols = cfg.H_kv * cfg.d_idx
+    flops = 2.0 * 2 * cfg.N * cfg.d_model * cols
+    # hidden read once, both outputs written, both weights read
+    nbytes = 2 * cfg.N * cfg.d_model + 2 * 2 * cfg.N * cols + 2 * 2 * cols * cfg.d_model
+    del t, q, k
+    return {"ms_per_step": round(ms, 3), "d_model": cfg.d_model,
+            "effective_tflops": round(flops / (ms / 1e3) / 1e12, 2),
+            "frac_bf16_peak": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "GB_per_s": round(nbytes / (ms / 1e3) / 1e9, 1), "bytes_per_step": nbytes}
+
+
 def cpu_baseline(cfg, t, n_rows):
     """The oracle, as it stands, on n_rows query rows spread over the sequence."""
     import numpy as np
@@ -406,6 +441,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra:
         extra = {f"index_kl_{cfg.name}": kl_leg, f"attn_bwd_{cfg.name}": bwd_leg}
+        log("[bench] index front-end leg")
+        extra[f"index_frontend_{cfg.name}"] = time_frontend(cfg)
+        torch.cuda.empty_cache()
         if cfg.name != "128k":
             c2 = CONFIGS["128k"]
             log("[bench] 128K prefill leg")

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["msa_api.hip", "index_topk.hip", "csr.hip", "attn.hip", "decode.hip", "kl.hip", "attn_bwd.hip"]
+SOURCES = ["msa_api.hip", "index_topk.hip", "csr.hip", "attn.hip", "decode.hip", "kl.hip", "attn_bwd.hip", "frontend.hip"]
 CFLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           # MFMA results in arch VGPRs: the epilogues read them with VALU ops

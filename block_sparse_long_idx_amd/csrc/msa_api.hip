@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 
 #include "../../include/msa.h"
@@ -416,6 +417,32 @@ msa_status msa_index_kl(const void* Q, const void* K, const void* q_idx, const v
                                        w.max_items, q_start, Nq, Nk, H_q, H_kv, d_h, d_idx, nblk,
                                        k, scale, w.part, kl, w.sums, kl_sum, s),
                   "index KL launch");
+  return st ? st : ok();
+}
+
+// ---------------------------------------------------------------- front-end
+msa_status msa_index_frontend(const void* hidden, const void* Wq, const void* Wk,
+                              const float* gq, const float* gk, int64_t N, int64_t pos0,
+                              int d_model, int H_kv, int d_idx, int rope_dim, float rope_theta,
+                              float eps, void* q_idx, void* k_idx, void* stream) {
+  if (!hidden || !Wq || !Wk || !gq || !gk || !q_idx || !k_idx)
+    return fail(MSA_ERR_INVALID_ARG, "null hidden, Wq, Wk, gq, gk, q_idx or k_idx");
+  if (N < 1 || pos0 < 0) return fail(MSA_ERR_INVALID_ARG, "need N >= 1 and pos0 >= 0");
+  if (N > ((int64_t)1 << 31) / 128) return fail(MSA_ERR_UNSUPPORTED, "N too large");
+  if (H_kv < 1 || H_kv > 64) return fail(MSA_ERR_INVALID_ARG, "H_kv must be in [1, 64]");
+  if (d_model < 64 || d_model % 64)
+    return fail(MSA_ERR_UNSUPPORTED, "d_model must be a positive multiple of 64 (got %d)", d_model);
+  if (d_idx != 32 && d_idx != 64 && d_idx != 128)
+    return fail(MSA_ERR_UNSUPPORTED, "d_idx must be 32, 64 or 128 (got %d)", d_idx);
+  if ((rope_dim != 0 && rope_dim != 32 && rope_dim != 64) || rope_dim > d_idx)
+    return fail(MSA_ERR_UNSUPPORTED, "rope_dim must be 0, 32 or 64 and <= d_idx (got %d)", rope_dim);
+  if (!(rope_theta > 1.f)) return fail(MSA_ERR_INVALID_ARG, "rope_theta must be > 1");
+  if (!(eps >= 0.f)) return fail(MSA_ERR_INVALID_ARG, "eps must be >= 0");
+  msa_status st = hip_status(
+      msa::launch_index_frontend(hidden, Wq, Wk, gq, gk, N, pos0, d_model, H_kv, d_idx,
+                                 rope_dim, std::log2((double)rope_theta), eps, q_idx, k_idx,
+                                 static_cast<hipStream_t>(stream)),
+      "front-end launch");
   return st ? st : ok();
 }
 

@@ -60,6 +60,13 @@ hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const fl
                            float* Dbuf, void* dq_part, float* kvpart, float* dQ, float* dK,
                            float* dV, hipStream_t stream);
 
+// frontend.hip
+hipError_t launch_index_frontend(const void* hidden, const void* Wq, const void* Wk,
+                                 const float* gq, const float* gk, int64_t N, int64_t pos0,
+                                 int d_model, int H_kv, int d_idx, int rope_dim,
+                                 double log2_theta, float eps, void* q_idx, void* k_idx,
+                                 hipStream_t stream);
+
 // kl.hip
 int64_t kl_sum_partials(int64_t n);
 hipError_t launch_index_kl(const void* Q, const void* K, const void* q_idx, const void* k_idx,

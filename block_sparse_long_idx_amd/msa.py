@@ -60,6 +60,8 @@ def load():
         "msa_index_kl_workspace_bytes": ([i64, i64, i32, i32, i32], sz),
         "msa_index_kl": ([P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32, i32, i32, i32,
                           i32, f32, P, P, P, sz, P], i32),
+        "msa_index_frontend": ([P, P, P, P, P, i64, i64, i32, i32, i32, i32, f32, f32, P, P,
+                                P], i32),
         "msa_sparse_attn_bwd_workspace_bytes": ([i64, i64, i32, i32, i32, i32, i32], sz),
         "msa_sparse_attn_bwd": ([P, P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32, i32,
                                  i32, i32, f32, P, P, P, P, sz, P], i32),
@@ -211,6 +213,24 @@ def sparse_attn_bwd(Q, K, V, O, lse, dO, row_ptr, col, slot, k, q_start=0, Nq=No
                                    H_kv, d_h, B_k, k, scale, _ptr(dQ), _ptr(dK), _ptr(dV),
                                    _ptr(ws), ws.numel(), _stream(Q)))
     return dQ, dK, dV
+
+
+def index_frontend(hidden, Wq, Wk, gq, gk, H_kv, d_idx, pos0=0, rope_dim=64,
+                   rope_theta=10000.0, eps=1e-6, q_idx=None, k_idx=None):
+    """Index Branch front-end: hidden [N, d_model] bf16 -> (q_idx, k_idx)
+    [N, H_kv, d_idx] bf16 by linear projection, per-group RMS norm and RoPE
+    over the first rope_dim entries at positions pos0 + i."""
+    _need_cuda(hidden, Wq, Wk, gq, gk)
+    N, d_model = hidden.shape
+    dev = hidden.device
+    if q_idx is None:
+        q_idx = torch.empty((N, H_kv, d_idx), dtype=torch.bfloat16, device=dev)
+    if k_idx is None:
+        k_idx = torch.empty((N, H_kv, d_idx), dtype=torch.bfloat16, device=dev)
+    _check(load().msa_index_frontend(_ptr(hidden), _ptr(Wq), _ptr(Wk), _ptr(gq), _ptr(gk), N,
+                                     pos0, d_model, H_kv, d_idx, min(rope_dim, d_idx),
+                                     rope_theta, eps, _ptr(q_idx), _ptr(k_idx), _stream(hidden)))
+    return q_idx, k_idx
 
 
 def index_kl_workspace_bytes(q_start, Nq, H_kv, k, B_k=B_K) -> int:

@@ -46,6 +46,7 @@ class MsaConfig:
     batch: int = 1               # decode: number of sequences
     decode: bool = False
     seed: int = 1000
+    d_model: int = 3072          # hidden width feeding the index front-end (section 06)
 
     @property
     def G(self) -> int:

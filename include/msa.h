@@ -230,6 +230,27 @@ msa_status msa_decode(const void *q, const void *q_idx, const void *K,
                       size_t ws_bytes, void *stream);
 
 /*
+ * Index Branch front-end (Figure 1 caption: the hidden states pass a
+ * linear projection and "Norm & RoPE" to give Q^idx and K^idx; section 06:
+ * RoPE width 64).  For token i at position pos0 + i and group r, with
+ * y = hidden[i] . W[r*d_idx : (r+1)*d_idx]^T (fp32 accumulation):
+ *   y <- y * gamma / sqrt(mean(y^2) + eps)           (RMS norm per group)
+ *   (y_j, y_{j+R/2}) <- rotation by (pos0+i) * theta^(-2j/R), j < R/2
+ * with R = rope_dim (rotate-half pairing; entries past R unchanged), then
+ * rounded to bf16.  Run once per projection (Wq -> q_idx, Wk -> k_idx).
+ *   hidden [N, d_model] bf16; Wq, Wk [H_kv*d_idx, d_model] bf16 (row r*d_idx+c
+ *   is output column c of group r); gq, gk [d_idx] fp32 norm scales
+ *   q_idx, k_idx out [N, H_kv, d_idx] bf16 (the Index Branch's inputs)
+ * d_model: a positive multiple of 64; d_idx in {32, 64, 128}; rope_dim in
+ * {0, 32, 64} and <= d_idx; rope_theta > 1; eps >= 0.  No workspace.
+ */
+msa_status msa_index_frontend(const void *hidden, const void *Wq, const void *Wk,
+                              const float *gq, const float *gk, int64_t N,
+                              int64_t pos0, int d_model, int H_kv, int d_idx,
+                              int rope_dim, float rope_theta, float eps,
+                              void *q_idx, void *k_idx, void *stream);
+
+/*
  * Tuning knobs (process-wide; they change speed, never results).
  *   MSA_OPT_INDEX_FUSED: 1 = Index Branch as one kernel that keeps a
  *     running Top-k per query next to the score GEMM; 0 = GEMM writes the

@@ -118,3 +118,22 @@ def test_options(lib):
     msa.set_option(msa.OPT_ATTN_CHUNK, 512)
     assert msa.get_option(msa.OPT_ATTN_CHUNK) == 512
     msa.set_option(msa.OPT_ATTN_CHUNK, old)
+
+
+@pytest.mark.parametrize("N,d_model,H_kv,d_idx,rope,theta,eps", [
+    (0, 256, 4, 64, 64, 1e4, 1e-6),        # no rows
+    (10, 96, 4, 64, 64, 1e4, 1e-6),        # d_model not a multiple of 64
+    (10, 256, 4, 48, 32, 1e4, 1e-6),       # unsupported d_idx
+    (10, 256, 4, 32, 64, 1e4, 1e-6),       # rope_dim > d_idx
+    (10, 256, 4, 64, 16, 1e4, 1e-6),       # unsupported rope_dim
+    (10, 256, 0, 64, 64, 1e4, 1e-6),       # no groups
+    (10, 256, 4, 64, 64, 1.0, 1e-6),       # theta <= 1
+    (10, 256, 4, 64, 64, 1e4, -1.0),       # negative eps
+])
+def test_frontend_rejects(lib, N, d_model, H_kv, d_idx, rope, theta, eps):
+    st = lib.msa_index_frontend(FAKE, FAKE, FAKE, FAKE, FAKE, N, 0, d_model, H_kv, d_idx, rope,
+                                theta, eps, FAKE, FAKE, NULL)
+    assert st != msa.OK
+    st = lib.msa_index_frontend(FAKE, NULL, FAKE, FAKE, FAKE, 10, 0, 256, 4, 64, 64, 1e4, 1e-6,
+                                FAKE, FAKE, NULL)
+    assert st == msa.ERR_INVALID_ARG
