@@ -190,7 +190,9 @@ struct TileRow {
 template <int DH>
 __device__ __forceinline__ TileRow tile_row(const AttnSmem<DH>& sm, int nrows, int tile, int r,
                                             int G, float inv_G, int n) {
-  TileRow t{0, 0, 0, false};
+  // rows past the end read the item's first query row (always in range,
+  // also when Q is addressed from the start of a cached-prefill chunk)
+  TileRow t{sm.pos[0], r * G, 0, false};
   const int R = tile * 32 + n;
   if (R < nrows) {
     const int p = (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G);
@@ -316,7 +318,9 @@ __device__ __forceinline__ void attn_item(const AttnSmem<DH>& sm, const __bf16* 
     }
     // ---- prefetch the next tile's Q into qb -----------------------------------
     const bool more = tile + 4 < ntile;
-    TileRow nrow[2] = {{0, 0, 0, false}, {0, 0, 0, false}};
+    // with no next tile the (unused) load still goes out: point it at the
+    // item's first query row, which is always in range
+    TileRow nrow[2] = {{sm.pos[0], r * G, 0, false}, {sm.pos[0], r * G, 0, false}};
     if (more) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)

@@ -183,13 +183,15 @@ struct PrefillWs {
   size_t bytes;
 };
 
-PrefillWs prefill_layout(void* ws, int64_t N, int64_t chunk, int H_q, int H_kv, int d_h, int k,
-                         bool own_sel) {
-  const int64_t nblk = cdiv(N, kB);
+// Workspace for the query positions [q_begin, q_end) of one sequence, in
+// chunks of `chunk` positions.
+PrefillWs prefill_layout(void* ws, int64_t q_begin, int64_t q_end, int64_t chunk, int H_q,
+                         int H_kv, int d_h, int k, bool own_sel) {
+  const int64_t nblk = cdiv(q_end, kB);
   int64_t nnz_max = 0;
   size_t shared = 0;
-  for (int64_t q0 = 0; q0 < N; q0 += chunk) {
-    const int64_t nq = std::min(chunk, N - q0);
+  for (int64_t q0 = q_begin; q0 < q_end; q0 += chunk) {
+    const int64_t nq = std::min(chunk, q_end - q0);
     nnz_max = std::max(nnz_max, nnz_of(q0, nq, H_kv, kB, k));
     shared = std::max(shared, index_ws(q0, nq, H_kv));
     shared = std::max(shared, invert_ws(q0, nq, H_kv));
@@ -204,6 +206,37 @@ PrefillWs prefill_layout(void* ws, int64_t N, int64_t chunk, int H_q, int H_kv, 
   w.shared = c.take<void>(shared);
   w.bytes = c.off;
   return w;
+}
+
+// The three stages over query positions [q_begin, q_end) of one sequence
+// whose keys are rows 0..Nk-1.  Q and q_idx are bases addressed by absolute
+// position (rows below q_begin are never touched); sel, O and lse point at
+// the row of position q_begin.
+msa_status prefill_span(const void* Q, const void* K, const void* V, const void* q_idx,
+                        const void* k_idx, int64_t q_begin, int64_t q_end, int64_t Nk,
+                        int64_t chunk, int H_q, int H_kv, int d_h, int d_idx, int k, float scale,
+                        int32_t* sel, float* O, float* lse, const PrefillWs& w, hipStream_t s) {
+  for (int64_t q0 = q_begin; q0 < q_end; q0 += chunk) {
+    const int64_t nq = std::min(chunk, q_end - q0), off = q0 - q_begin;
+    int32_t* sel_c = sel ? sel + off * H_kv * k : w.sel;
+    msa_status st = run_index_topk(q_idx, k_idx, q0, nq, H_kv, d_idx, k, sel_c, w.shared, s);
+    if (st) return st;
+    const int nblk = (int)cdiv(q0 + nq, kB);
+    st = hip_status(msa::launch_invert(sel_c, q0, nq, H_kv, k, nblk, w.row_ptr, w.col, w.slot,
+                                       w.shared, s),
+                    "inverted-index launch");
+    if (st) return st;
+    st = run_attn(Q, K, V, w.row_ptr, w.col, w.slot, q0, nq, Nk, H_q, H_kv, d_h, k, scale,
+                  O + off * H_q * d_h, lse ? lse + off * H_q : nullptr, w.shared, s);
+    if (st) return st;
+  }
+  return MSA_OK;
+}
+
+// A base pointer for rows addressed by absolute position when the buffer
+// starts at row `first` (only rows >= first are ever read through it).
+const void* row_base(const void* p, int64_t first, int64_t row_elems, size_t elem) {
+  return static_cast<const char*>(p) - first * row_elems * (int64_t)elem;
 }
 
 // ---------------------------------------------------------------- decode
@@ -452,7 +485,7 @@ size_t msa_prefill_workspace_bytes(int64_t N, int64_t chunk, int H_q, int H_kv, 
   if (N < 1) return 0;
   if (chunk <= 0 || chunk > N) chunk = N;
   if (check_common(0, N, H_kv, B_k, k) || check_attn_shapes(H_q, H_kv, d_h)) return 0;
-  return prefill_layout(nullptr, N, chunk, H_q, H_kv, d_h, k, true).bytes;
+  return prefill_layout(nullptr, 0, N, chunk, H_q, H_kv, d_h, k, true).bytes;
 }
 
 msa_status msa_prefill(const void* Q, const void* K, const void* V, const void* q_idx,
@@ -469,22 +502,116 @@ msa_status msa_prefill(const void* Q, const void* K, const void* V, const void* 
     return fail(MSA_ERR_INVALID_ARG, "null Q, K, V, q_idx, k_idx or O");
   if (!(scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "scale must be > 0");
   const bool own_sel = sel == nullptr;
-  const size_t need = prefill_layout(nullptr, N, chunk, H_q, H_kv, d_h, k, true).bytes;
+  const size_t need = prefill_layout(nullptr, 0, N, chunk, H_q, H_kv, d_h, k, true).bytes;
   if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
-  PrefillWs w = prefill_layout(ws, N, chunk, H_q, H_kv, d_h, k, own_sel);
+  PrefillWs w = prefill_layout(ws, 0, N, chunk, H_q, H_kv, d_h, k, own_sel);
+  msa_status st = prefill_span(Q, K, V, q_idx, k_idx, 0, N, N, chunk, H_q, H_kv, d_h, d_idx, k,
+                               scale, sel, O, lse, w, static_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+size_t msa_prefill_cached_workspace_bytes(int64_t q_start, int64_t Nq, int64_t chunk, int H_q,
+                                          int H_kv, int d_h, int d_idx, int B_k, int k) {
+  (void)d_idx;
+  if (chunk < 0 || check_common(q_start, Nq, H_kv, B_k, k) || check_attn_shapes(H_q, H_kv, d_h))
+    return 0;
+  if (chunk == 0 || chunk > Nq) chunk = Nq;
+  return prefill_layout(nullptr, q_start, q_start + Nq, chunk, H_q, H_kv, d_h, k, true).bytes;
+}
+
+msa_status msa_prefill_cached(const void* Q, const void* K, const void* V, const void* q_idx,
+                              const void* k_idx, int64_t q_start, int64_t Nq, int64_t chunk,
+                              int H_q, int H_kv, int d_h, int d_idx, int B_k, int k, float scale,
+                              int32_t* sel, float* O, float* lse, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (chunk < 0) return fail(MSA_ERR_INVALID_ARG, "chunk must be >= 0");
+  if (msa_status st = check_common(q_start, Nq, H_kv, B_k, k)) return st;
+  if (msa_status st = check_attn_shapes(H_q, H_kv, d_h)) return st;
+  if (msa_status st = check_index_dims(d_idx)) return st;
+  if (!Q || !K || !V || !q_idx || !k_idx || !O)
+    return fail(MSA_ERR_INVALID_ARG, "null Q, K, V, q_idx, k_idx or O");
+  if (!(scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "scale must be > 0");
+  if (chunk == 0 || chunk > Nq) chunk = Nq;
+  const int64_t q_end = q_start + Nq;
+  const bool own_sel = sel == nullptr;
+  const size_t need = prefill_layout(nullptr, q_start, q_end, chunk, H_q, H_kv, d_h, k, true).bytes;
+  if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  PrefillWs w = prefill_layout(ws, q_start, q_end, chunk, H_q, H_kv, d_h, k, own_sel);
+  msa_status st = prefill_span(row_base(Q, q_start, (int64_t)H_q * d_h, 2), K, V,
+                               row_base(q_idx, q_start, (int64_t)H_kv * d_idx, 2), k_idx,
+                               q_start, q_end, q_end, chunk, H_q, H_kv, d_h, d_idx, k, scale,
+                               sel, O, lse, w, static_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+// Sequences of a varlen batch, validated: lengths from the host prefix sums.
+msa_status check_cu_seqlens(const int64_t* cu, int B) {
+  if (!cu || B < 1) return fail(MSA_ERR_INVALID_ARG, "need cu_seqlens and B >= 1");
+  if (cu[0] != 0) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+  for (int b = 0; b < B; ++b)
+    if (cu[b + 1] < cu[b]) return fail(MSA_ERR_INVALID_ARG, "cu_seqlens must be nondecreasing");
+  if (cu[B] < 1) return fail(MSA_ERR_INVALID_ARG, "the batch holds no tokens");
+  return MSA_OK;
+}
+
+size_t varlen_bytes(const int64_t* cu, int B, int64_t chunk, int H_q, int H_kv, int d_h, int k) {
+  size_t need = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t L = cu[b + 1] - cu[b];
+    if (L < 1) continue;
+    const int64_t c = (chunk == 0 || chunk > L) ? L : chunk;
+    need = std::max(need, prefill_layout(nullptr, 0, L, c, H_q, H_kv, d_h, k, true).bytes);
+  }
+  return need;
+}
+
+size_t msa_prefill_varlen_workspace_bytes(const int64_t* cu_seqlens, int B, int64_t chunk,
+                                          int H_q, int H_kv, int d_h, int d_idx, int B_k, int k) {
+  (void)d_idx;
+  if (chunk < 0 || check_cu_seqlens(cu_seqlens, B)) return 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t L = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (L > 0 && check_common(0, L, H_kv, B_k, k)) return 0;
+  }
+  if (check_attn_shapes(H_q, H_kv, d_h)) return 0;
+  return varlen_bytes(cu_seqlens, B, chunk, H_q, H_kv, d_h, k);
+}
+
+msa_status msa_prefill_varlen(const void* Q, const void* K, const void* V, const void* q_idx,
+                              const void* k_idx, const int64_t* cu_seqlens, int B, int64_t chunk,
+                              int H_q, int H_kv, int d_h, int d_idx, int B_k, int k, float scale,
+                              int32_t* sel, float* O, float* lse, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (chunk < 0) return fail(MSA_ERR_INVALID_ARG, "chunk must be >= 0");
+  if (msa_status st = check_cu_seqlens(cu_seqlens, B)) return st;
+  for (int b = 0; b < B; ++b) {
+    const int64_t L = cu_seqlens[b + 1] - cu_seqlens[b];
+    if (L < 1) continue;
+    if (msa_status st = check_common(0, L, H_kv, B_k, k)) return st;
+  }
+  if (msa_status st = check_attn_shapes(H_q, H_kv, d_h)) return st;
+  if (msa_status st = check_index_dims(d_idx)) return st;
+  if (!Q || !K || !V || !q_idx || !k_idx || !O)
+    return fail(MSA_ERR_INVALID_ARG, "null Q, K, V, q_idx, k_idx or O");
+  if (!(scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "scale must be > 0");
+  const size_t need = varlen_bytes(cu_seqlens, B, chunk, H_q, H_kv, d_h, k);
+  if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  for (int64_t q0 = 0; q0 < N; q0 += chunk) {
-    const int64_t nq = std::min(chunk, N - q0);
-    int32_t* sel_c = own_sel ? w.sel : sel + q0 * H_kv * k;
-    msa_status st = run_index_topk(q_idx, k_idx, q0, nq, H_kv, d_idx, k, sel_c, w.shared, s);
-    if (st) return st;
-    const int nblk = (int)cdiv(q0 + nq, kB);
-    st = hip_status(msa::launch_invert(sel_c, q0, nq, H_kv, k, nblk, w.row_ptr, w.col, w.slot,
-                                       w.shared, s),
-                    "inverted-index launch");
-    if (st) return st;
-    st = run_attn(Q, K, V, w.row_ptr, w.col, w.slot, q0, nq, N, H_q, H_kv, d_h, k, scale,
-                  O + q0 * H_q * d_h, lse ? lse + q0 * H_q : nullptr, w.shared, s);
+  const bool own_sel = sel == nullptr;
+  auto at = [](const void* p, int64_t row, int64_t row_elems) {
+    return static_cast<const char*>(p) + row * row_elems * 2;
+  };
+  for (int b = 0; b < B; ++b) {
+    const int64_t t0 = cu_seqlens[b], L = cu_seqlens[b + 1] - t0;
+    if (L < 1) continue;
+    const int64_t c = (chunk == 0 || chunk > L) ? L : chunk;
+    PrefillWs w = prefill_layout(ws, 0, L, c, H_q, H_kv, d_h, k, own_sel);
+    msa_status st = prefill_span(
+        at(Q, t0, (int64_t)H_q * d_h), at(K, t0, (int64_t)H_kv * d_h),
+        at(V, t0, (int64_t)H_kv * d_h), at(q_idx, t0, (int64_t)H_kv * d_idx),
+        at(k_idx, t0, (int64_t)H_kv * d_idx), 0, L, L, c, H_q, H_kv, d_h, d_idx, k, scale,
+        own_sel ? nullptr : sel + t0 * H_kv * k, O + t0 * H_q * d_h,
+        lse ? lse + t0 * H_q : nullptr, w, s);
     if (st) return st;
   }
   return ok();

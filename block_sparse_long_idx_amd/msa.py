@@ -60,6 +60,13 @@ def load():
         "msa_index_kl_workspace_bytes": ([i64, i64, i32, i32, i32], sz),
         "msa_index_kl": ([P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32, i32, i32, i32,
                           i32, f32, P, P, P, sz, P], i32),
+        "msa_prefill_cached_workspace_bytes": ([i64, i64, i64, i32, i32, i32, i32, i32, i32],
+                                               sz),
+        "msa_prefill_cached": ([P, P, P, P, P, i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                f32, P, P, P, P, sz, P], i32),
+        "msa_prefill_varlen_workspace_bytes": ([P, i32, i64, i32, i32, i32, i32, i32, i32], sz),
+        "msa_prefill_varlen": ([P, P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32, f32,
+                                P, P, P, P, sz, P], i32),
         "msa_index_frontend": ([P, P, P, P, P, i64, i64, i32, i32, i32, i32, f32, f32, P, P,
                                 P], i32),
         "msa_sparse_attn_bwd_workspace_bytes": ([i64, i64, i32, i32, i32, i32, i32], sz),
@@ -213,6 +220,63 @@ def sparse_attn_bwd(Q, K, V, O, lse, dO, row_ptr, col, slot, k, q_start=0, Nq=No
                                    H_kv, d_h, B_k, k, scale, _ptr(dQ), _ptr(dK), _ptr(dV),
                                    _ptr(ws), ws.numel(), _stream(Q)))
     return dQ, dK, dV
+
+
+def prefill_cached(Q, K, V, q_idx, k_idx, k, q_start, chunk=0, scale=None, B_k=B_K,
+                   sel=None, O=None, lse=None, want_lse=True, ws=None):
+    """Chunked prefill against a KV cache: Q/q_idx hold the Nq new tokens
+    (positions q_start..), K/V/k_idx the cache with them appended.
+    Returns (sel, O, lse) for the new tokens."""
+    _need_cuda(Q, K, V, q_idx, k_idx)
+    Nq, H_q, d_h = Q.shape
+    H_kv, d_idx = k_idx.shape[1], k_idx.shape[2]
+    if K.shape[0] < q_start + Nq or k_idx.shape[0] < q_start + Nq:
+        raise ValueError("the cache must hold q_start + Nq keys")
+    scale = 1.0 / math.sqrt(d_h) if scale is None else scale
+    lib = load()
+    dev = Q.device
+    if sel is None:
+        sel = torch.empty((Nq, H_kv, k), dtype=torch.int32, device=dev)
+    if O is None:
+        O = torch.empty((Nq, H_q, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((Nq, H_q), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(lib.msa_prefill_cached_workspace_bytes(q_start, Nq, chunk, H_q, H_kv,
+                                                               d_h, d_idx, B_k, k), dev)
+    _check(lib.msa_prefill_cached(_ptr(Q), _ptr(K), _ptr(V), _ptr(q_idx), _ptr(k_idx), q_start,
+                                  Nq, chunk, H_q, H_kv, d_h, d_idx, B_k, k, scale, _ptr(sel),
+                                  _ptr(O), _ptr(lse), _ptr(ws), ws.numel(), _stream(Q)))
+    return sel, O, lse
+
+
+def prefill_varlen(Q, K, V, q_idx, k_idx, cu_seqlens, k, chunk=0, scale=None, B_k=B_K,
+                   sel=None, O=None, lse=None, want_lse=True, ws=None):
+    """Varlen batched prefill of packed sequences; cu_seqlens is a host
+    sequence of B+1 prefix sums.  Returns (sel, O, lse) for all tokens."""
+    _need_cuda(Q, K, V, q_idx, k_idx)
+    T, H_q, d_h = Q.shape
+    H_kv, d_idx = k_idx.shape[1], k_idx.shape[2]
+    cu = (ctypes.c_int64 * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
+    B = len(cu_seqlens) - 1
+    if int(cu_seqlens[-1]) != T:
+        raise ValueError("cu_seqlens[-1] must equal the number of packed tokens")
+    scale = 1.0 / math.sqrt(d_h) if scale is None else scale
+    lib = load()
+    dev = Q.device
+    if sel is None:
+        sel = torch.empty((T, H_kv, k), dtype=torch.int32, device=dev)
+    if O is None:
+        O = torch.empty((T, H_q, d_h), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H_q), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(lib.msa_prefill_varlen_workspace_bytes(cu, B, chunk, H_q, H_kv, d_h,
+                                                               d_idx, B_k, k), dev)
+    _check(lib.msa_prefill_varlen(_ptr(Q), _ptr(K), _ptr(V), _ptr(q_idx), _ptr(k_idx), cu, B,
+                                  chunk, H_q, H_kv, d_h, d_idx, B_k, k, scale, _ptr(sel),
+                                  _ptr(O), _ptr(lse), _ptr(ws), ws.numel(), _stream(Q)))
+    return sel, O, lse
 
 
 def index_frontend(hidden, Wq, Wk, gq, gk, H_kv, d_idx, pos0=0, rope_dim=64,

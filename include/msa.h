@@ -147,6 +147,50 @@ msa_status msa_prefill(const void *Q, const void *K, const void *V,
                        float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Chunked prefill against a KV cache: the Nq new tokens at positions
+ * q_start .. q_start+Nq-1 attend causally to the cached tokens and to each
+ * other, exactly as rows q_start.. of msa_prefill over the whole sequence
+ * (each row depends only on its own prefix).
+ *   Q [Nq, H_q, d_h], q_idx [Nq, H_kv, d_idx]: the new tokens only
+ *   K, V [q_start+Nq, H_kv, d_h], k_idx [q_start+Nq, H_kv, d_idx]: the
+ *     cache with the new tokens' keys already appended
+ *   sel out [Nq, H_kv, k] int32 (nullable), O out [Nq, H_q, d_h] fp32,
+ *   lse out [Nq, H_q] fp32 (nullable)
+ * chunk: query positions per internal pass (0 = all Nq at once).
+ */
+size_t msa_prefill_cached_workspace_bytes(int64_t q_start, int64_t Nq, int64_t chunk,
+                                          int H_q, int H_kv, int d_h, int d_idx,
+                                          int B_k, int k);
+msa_status msa_prefill_cached(const void *Q, const void *K, const void *V,
+                              const void *q_idx, const void *k_idx, int64_t q_start,
+                              int64_t Nq, int64_t chunk, int H_q, int H_kv, int d_h,
+                              int d_idx, int B_k, int k, float scale, int32_t *sel,
+                              float *O, float *lse, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/*
+ * Varlen batched prefill: B independent sequences packed token-major.
+ * Sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of every tensor,
+ * with its own positions 0..L_b-1 and its own causal prefix; it gets the
+ * msa_prefill result of that sequence alone.  Sequences run one after
+ * another on the stream, each in query chunks of `chunk` (0 = whole).
+ *   cu_seqlens: HOST array of B+1 prefix sums, cu_seqlens[0] = 0,
+ *     nondecreasing (empty sequences are skipped), cu_seqlens[B] >= 1
+ *   Q [T, H_q, d_h], K, V [T, H_kv, d_h], q_idx, k_idx [T, H_kv, d_idx]
+ *   bf16, T = cu_seqlens[B]; sel out [T, H_kv, k] (nullable), O out
+ *   [T, H_q, d_h] fp32, lse out [T, H_q] (nullable)
+ */
+size_t msa_prefill_varlen_workspace_bytes(const int64_t *cu_seqlens, int B, int64_t chunk,
+                                          int H_q, int H_kv, int d_h, int d_idx,
+                                          int B_k, int k);
+msa_status msa_prefill_varlen(const void *Q, const void *K, const void *V,
+                              const void *q_idx, const void *k_idx,
+                              const int64_t *cu_seqlens, int B, int64_t chunk, int H_q,
+                              int H_kv, int d_h, int d_idx, int B_k, int k, float scale,
+                              int32_t *sel, float *O, float *lse, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/*
  * Main Branch backward (section 02: exact softmax attention over the
  * selected blocks, so its gradients are those of softmax attention on each
  * row's token set; section 03: the selection is not differentiable, so no

@@ -137,3 +137,22 @@ def test_frontend_rejects(lib, N, d_model, H_kv, d_idx, rope, theta, eps):
     st = lib.msa_index_frontend(FAKE, NULL, FAKE, FAKE, FAKE, 10, 0, 256, 4, 64, 64, 1e4, 1e-6,
                                 FAKE, FAKE, NULL)
     assert st == msa.ERR_INVALID_ARG
+
+
+def test_varlen_and_cached_reject(lib):
+    bad = [(0, 5, 3), (0, 5, 3, 2), (1, 5), (0, 0)]   # decreasing, cu[0] != 0, no tokens
+    for cu in bad:
+        arr = (ctypes.c_int64 * len(cu))(*cu)
+        B = len(cu) - 1
+        assert lib.msa_prefill_varlen_workspace_bytes(arr, B, 0, 16, 4, 128, 64, 128, 8) == 0
+        st = lib.msa_prefill_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, arr, B, 0, 16, 4, 128, 64,
+                                    128, 8, 0.1, NULL, FAKE, NULL, FAKE, 1 << 30, NULL)
+        assert st == msa.ERR_INVALID_ARG
+    arr = (ctypes.c_int64 * 3)(0, 100, 300)
+    assert lib.msa_prefill_varlen_workspace_bytes(arr, 2, 0, 16, 4, 128, 64, 128, 8) > 0
+    # the cached form validates like the stage calls
+    assert lib.msa_prefill_cached_workspace_bytes(1000, 500, 0, 16, 4, 128, 64, 128, 8) > 0
+    assert lib.msa_prefill_cached_workspace_bytes(-1, 500, 0, 16, 4, 128, 64, 128, 8) == 0
+    st = lib.msa_prefill_cached(FAKE, FAKE, FAKE, FAKE, FAKE, 1000, 0, 0, 16, 4, 128, 64, 128, 8,
+                                0.1, NULL, FAKE, NULL, FAKE, 1 << 30, NULL)
+    assert st == msa.ERR_INVALID_ARG
