@@ -10,8 +10,8 @@ Prints one JSON line: prefill tokens/s (value), effective TFLOP/s by the
 MSA FLOP formula 4*H_q*d_h*N*k*B_k + H_kv*d_idx*N^2 (as a fraction of the
 2.5 PFLOP/s bf16 MFMA peak), per-stage times, the roofline of the dominant
 kernel, the CPU oracle timed on sampled rows, and the index-alignment KL
-pass, Main Branch backward, index front-end, 128K-prefill and 32 x 1M
-decode figures.
+pass, Main Branch backward, cached and varlen prefill, index front-end,
+128K-prefill and 32 x 1M decode figures.
 """
 import argparse
 import json
@@ -284,6 +284,97 @@ def time_frontend(cfg, reps=3):
             "GB_per_s": round(nbytes / (ms / 1e3) / 1e9, 1), "bytes_per_step": nbytes}
 
 
+VARLEN_FRACTIONS = (3 / 8, 1 / 4, 1 / 8, 1 / 8, 1 / 16, 1 / 32, 1 / 64, 1 / 64)
+
+
+def time_cached(cfg, t, reps=3):
+    """Chunked prefill against a KV cache: the last query chunk of the
+    sequence (its own Q/q_idx rows only) against the cache of all keys."""
+    import torch
+    from block_sparse_long_idx_amd import msa
+    c = cfg.chunk or cfg.N
+    q0 = cfg.N - c
+    Qc, qic = t["Q"][q0:], t["q_idx"][q0:]
+    lib = msa.load()
+    ws = torch.empty(lib.msa_prefill_cached_workspace_bytes(q0, c, 0, cfg.H_q, cfg.H_kv, cfg.d_h,
+                                                            cfg.d_idx, cfg.B_k, cfg.k),
+                     dtype=torch.uint8, device="cuda")
+    sel = torch.empty((c, cfg.H_kv, cfg.k), dtype=torch.int32, device="cuda")
+    O = torch.empty((c, cfg.H_q, cfg.d_h), dtype=torch.float32, device="cuda")
+    lse = torch.empty((c, cfg.H_q), dtype=torch.float32, device="cuda")
+
+    def run():
+        msa.prefill_cached(Qc, t["K"], t["V"], qic, t["k_idx"], cfg.k, q_start=q0,
+                           scale=cfg.scale, sel=sel, O=O, lse=lse, ws=ws)
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del ws, sel, O, lse
+    return {"new_tokens": c, "cached_tokens": q0, "ms": round(ms, 3),
+            "tokens_per_s": round(c / (ms / 1e3), 1)}
+
+
+def time_varlen(cfg, reps=2):
+    """Varlen batched prefill: eight packed sequences whose lengths sum to
+    N (fractions VARLEN_FRACTIONS), each with its own positions and prefix."""
+    import torch
+    from block_sparse_long_idx_amd import msa
+    from block_sparse_long_idx_amd.synth import make_prefill_inputs
+    lens = [int(cfg.N * f) for f in VARLEN_FRACTIONS]
+    lens[0] += cfg.N - sum(lens)
+    packed = None
+    for b, L in enumerate(lens):
+        s = make_prefill_inputs(L, cfg.H_q, cfg.H_kv, cfg.d_h, cfg.d_idx,
+                                n_hot=max(1, cfg.n_hot * L // cfg.N), seed=cfg.seed + 100 + b,
+                                device="cuda")
+        if packed is None:
+            packed = {key: torch.empty((cfg.N,) + v.shape[1:], dtype=v.dtype, device="cuda")
+                      for key, v in s.items()}
+        t0 = sum(lens[:b])
+        for key, v in s.items():
+            packed[key][t0:t0 + L] = v
+        del s
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    chunk = cfg.chunk or 0
+    lib = msa.load()
+    import ctypes
+    cua = (ctypes.c_int64 * len(cu))(*cu)
+    ws = torch.empty(lib.msa_prefill_varlen_workspace_bytes(cua, len(lens), chunk, cfg.H_q,
+                                                            cfg.H_kv, cfg.d_h, cfg.d_idx,
+                                                            cfg.B_k, cfg.k),
+                     dtype=torch.uint8, device="cuda")
+    O = torch.empty((cfg.N, cfg.H_q, cfg.d_h), dtype=torch.float32, device="cuda")
+
+    def run():
+        msa.prefill_varlen(packed["Q"], packed["K"], packed["V"], packed["q_idx"],
+                           packed["k_idx"], cu, cfg.k, chunk=chunk, scale=cfg.scale,
+                           want_lse=False, sel=None, O=O, ws=ws)
+    run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        run()
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = sum(4.0 * cfg.H_q * cfg.d_h * L * cfg.k * cfg.B_k + float(cfg.H_kv) * cfg.d_idx * L * L
+                for L in lens)
+    del packed, ws, O
+    return {"lengths": lens, "ms_per_step": round(ms, 3),
+            "tokens_per_s": round(cfg.N / (ms / 1e3), 1),
+            "effective_tflops": round(flops / (ms / 1e3) / 1e12, 2),
+            "frac_bf16_peak": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def cpu_baseline(cfg, t, n_rows):
     """The oracle, as it stands, on n_rows query rows spread over the sequence."""
     import numpy as np
@@ -431,16 +522,22 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on {args.cpu_rows} sampled rows")
         out["cpu_baseline"] = cpu_baseline(cfg, t, args.cpu_rows)
-    kl_leg = bwd_leg = None
+    kl_leg = bwd_leg = cached_leg = None
     if not args.no_extra:
         log("[bench] index KL leg")
         kl_leg = time_kl(pf, cfg, t)
         log("[bench] Main Branch backward leg")
         bwd_leg = time_bwd(pf, cfg, t)
+        log("[bench] cached-prefill leg")
+        cached_leg = time_cached(cfg, t)
     del pf, t
     torch.cuda.empty_cache()
     if not args.no_extra:
-        extra = {f"index_kl_{cfg.name}": kl_leg, f"attn_bwd_{cfg.name}": bwd_leg}
+        extra = {f"index_kl_{cfg.name}": kl_leg, f"attn_bwd_{cfg.name}": bwd_leg,
+                 f"prefill_cached_{cfg.name}": cached_leg}
+        log("[bench] varlen batch leg")
+        extra[f"prefill_varlen_{cfg.name}"] = time_varlen(cfg)
+        torch.cuda.empty_cache()
         log("[bench] index front-end leg")
         extra[f"index_frontend_{cfg.name}"] = time_frontend(cfg)
         torch.cuda.empty_cache()
