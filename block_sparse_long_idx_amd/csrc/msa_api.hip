@@ -216,11 +216,24 @@ msa_status prefill_span(const void* Q, const void* K, const void* V, const void*
                         const void* k_idx, int64_t q_begin, int64_t q_end, int64_t Nk,
                         int64_t chunk, int H_q, int H_kv, int d_h, int d_idx, int k, float scale,
                         int32_t* sel, float* O, float* lse, const PrefillWs& w, hipStream_t s) {
+  // The fused Index Branch keeps no per-chunk state, so when the caller's
+  // sel holds the whole span it runs once over all of it: its work-groups,
+  // heaviest first, then balance across what would be separate chunk
+  // launches (the early chunks alone leave most of the GPU idle).
+  const bool whole_index = g_opt_fused && sel != nullptr;
+  if (whole_index) {
+    msa_status st =
+        run_index_topk(q_idx, k_idx, q_begin, q_end - q_begin, H_kv, d_idx, k, sel, nullptr, s);
+    if (st) return st;
+  }
   for (int64_t q0 = q_begin; q0 < q_end; q0 += chunk) {
     const int64_t nq = std::min(chunk, q_end - q0), off = q0 - q_begin;
     int32_t* sel_c = sel ? sel + off * H_kv * k : w.sel;
-    msa_status st = run_index_topk(q_idx, k_idx, q0, nq, H_kv, d_idx, k, sel_c, w.shared, s);
-    if (st) return st;
+    if (!whole_index) {
+      msa_status st = run_index_topk(q_idx, k_idx, q0, nq, H_kv, d_idx, k, sel_c, w.shared, s);
+      if (st) return st;
+    }
+    msa_status st;
     const int nblk = (int)cdiv(q0 + nq, kB);
     st = hip_status(msa::launch_invert(sel_c, q0, nq, H_kv, k, nblk, w.row_ptr, w.col, w.slot,
                                        w.shared, s),
