@@ -72,7 +72,7 @@ def chunks_of(cfg):
 class Prefill:
     """Preallocated buffers and the per-chunk call sequence of one step."""
 
-    def __init__(self, cfg, t):
+    def __init__(self, cfg, t, whole_index=True):
         import torch
         from block_sparse_long_idx_amd import msa
         self.cfg, self.t, self.msa = cfg, t, msa
@@ -87,7 +87,7 @@ class Prefill:
                 q0, nq, cfg.H_q, cfg.H_kv, cfg.d_h, cfg.B_k, cfg.k))
             nnz = max(nnz, msa.selection_nnz(q0, nq, cfg.H_kv, cfg.k))
         fused = msa.get_option(msa.OPT_INDEX_FUSED)
-        self.whole_index = bool(fused)
+        self.whole_index = bool(fused) and whole_index
         u8 = torch.uint8
         self.ws_i = torch.empty(1 if fused else ws_i, dtype=u8, device=dev)
         self.ws_v = torch.empty(ws_v, dtype=u8, device=dev)
@@ -152,9 +152,9 @@ class Prefill:
         return tot
 
 
-def time_prefill(cfg, t, steps, warmup):
+def time_prefill(cfg, t, steps, warmup, whole_index=True):
     import torch
-    pf = Prefill(cfg, t)
+    pf = Prefill(cfg, t, whole_index)
     for _ in range(warmup):
         pf.step()
     torch.cuda.synchronize()
@@ -464,6 +464,8 @@ def main():
     ap.add_argument("--workload", default="1m", choices=["tiny", "8k", "128k", "1m"])
     ap.add_argument("--fused", type=int, default=1, help="fused Index-Branch kernel (1/0)")
     ap.add_argument("--attn-chunk", type=int, default=0, help="positions per work item")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="query positions per Main Branch pass (0 = the workload's)")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 128K and decode legs")
@@ -493,6 +495,9 @@ def main():
     if args.attn_chunk:
         msa.set_option(msa.OPT_ATTN_CHUNK, args.attn_chunk)
     cfg = CONFIGS[args.workload]
+    if args.chunk:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, chunk=args.chunk)
     log(f"[bench] workload {cfg.name}: generating inputs on the GPU")
     t = inputs_for(cfg, device="cuda")
     torch.cuda.synchronize()
@@ -531,6 +536,7 @@ def main():
                    "H_kv": cfg.H_kv, "d_h": cfg.d_h, "d_idx": cfg.d_idx, "k": cfg.k,
                    "B_k": cfg.B_k, "query_chunk": cfg.chunk or cfg.N,
                    "index_variant": "fused" if args.fused else "two-kernel",
+                   "index_launch": "whole sequence" if args.fused else "per query chunk",
                    "attn_chunk": msa.get_option(msa.OPT_ATTN_CHUNK)},
         "effective_tflops": round(tflops, 2),
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -542,7 +548,13 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on {args.cpu_rows} sampled rows")
         out["cpu_baseline"] = cpu_baseline(cfg, t, args.cpu_rows)
-    kl_leg = bwd_leg = cached_leg = None
+    kl_leg = bwd_leg = cached_leg = chunked_leg = None
+    if not args.no_extra and args.fused:
+        log("[bench] per-chunk index leg")
+        _, ms_c, st_c = time_prefill(cfg, t, 2, 1, whole_index=False)
+        chunked_leg = {"ms_per_step": round(ms_c, 3),
+                       "tokens_per_s": round(cfg.N / (ms_c / 1e3), 1),
+                       "stage_ms": {n: round(x, 3) for n, x in zip(stage_names, st_c)}}
     if not args.no_extra:
         log("[bench] index KL leg")
         kl_leg = time_kl(pf, cfg, t)
@@ -555,6 +567,8 @@ def main():
     if not args.no_extra:
         extra = {f"index_kl_{cfg.name}": kl_leg, f"attn_bwd_{cfg.name}": bwd_leg,
                  f"prefill_cached_{cfg.name}": cached_leg}
+        if chunked_leg:
+            extra[f"prefill_{cfg.name}_index_per_chunk"] = chunked_leg
         log("[bench] varlen batch leg")
         extra[f"prefill_varlen_{cfg.name}"] = time_varlen(cfg)
         torch.cuda.empty_cache()
