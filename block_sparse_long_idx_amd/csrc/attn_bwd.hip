@@ -147,9 +147,11 @@ template <int DH>
 struct BwdSmem {
   __bf16 qr[2][32 * DH];    // the tile's Q rows, row-major swizzled
   __bf16 gr[2][32 * DH];    // the tile's dO rows
-  __bf16 qt[2][DH * kRp];   // the same, transposed [d][row]
-  __bf16 gt[2][DH * kRp];
-  __bf16 ds[2][32 * kDsp];  // dS [row][key]
+  __bf16 qt[3][DH * kRp];   // the same, transposed [d][row] (three tiles live)
+  __bf16 gt[3][DH * kRp];
+  __bf16 ds[2][32 * kDsp];  // dS [row][key], for dQ
+  __bf16 pt[2][kBlock * kRp];   // P^T [key][row], for the second d-half's dV
+  __bf16 dst[2][kBlock * kRp];  // dS^T [key][row], for its dK
   int32_t lim[2][32];       // per tile row: last visible key of the block (-1: none)
   float l2[2][32];          // lse * log2(e)
   float dv[2][32];          // D = dO . O
@@ -157,10 +159,20 @@ struct BwdSmem {
   uint8_t sl[kUnitPos];     // and the block's slot in each one's selection
 };
 
-// One work-group per CU (its LDS), so the register budget is one wave per
-// SIMD: the scheduler may spend it on keeping LDS reads ahead of the MFMAs.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// Eight waves per work-group, two per SIMD, in producer/consumer pairs
+// over the same 32 keys kw = 32 (w mod 4):
+//  - waves 0-3 (first d-half) form S = Q K^T and dP = dO V^T, the softmax
+//    and dS for tile T, add its P^T dO and dS^T Q into dV/dK for d < DH/2,
+//    and leave dS, P^T and dS^T in LDS;
+//  - waves 4-7 take tile T-1 from LDS after the barrier: dV/dK for the
+//    second d-half, and dQ^T = K^T dS^T for their 32-wide d-slice (K^T in
+//    registers).
+// No MFMA or softmax is done twice, and each SIMD holds one wave of each
+// kind, so one's softmax and LDS waits overlap the other's MFMAs.
 template <int DH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_fused_kernel(
+__global__ __launch_bounds__(512) void bwd_fused_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ D,
     const int32_t* __restrict__ col, const uint8_t* __restrict__ slot,
@@ -168,7 +180,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int H_q, int H_kv, int G, float inv_G, int nblk, int k, int64_t spare, float scale,
     float scale_log2, __bf16* __restrict__ part, float* __restrict__ kvpart,
     float* __restrict__ dK, float* __restrict__ dV) {
-  constexpr int S = DH / 16, NDG = DH / 32, CH = DH / 8;
+  constexpr int S = DH / 16, NDG = DH / 32, NDH = NDG / 2, CH = DH / 8;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   BwdSmem<DH>& sm = *reinterpret_cast<BwdSmem<DH>*>(smem_raw);
   __shared__ int32_t next;
@@ -185,18 +197,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int tl = t;  // per-unit addresses are rebuilt, not hoisted and spilled
     asm volatile("" : "+v"(tl));
     {
-      // count <= kUnitPos = 4 * 256: all loads first, then the LDS stores
-      int32_t pv[kUnitPos / 256];
-      uint8_t sv[kUnitPos / 256];
+      // count <= kUnitPos = 2 * 512: all loads first, then the LDS stores
+      int32_t pv[kUnitPos / 512];
+      uint8_t sv[kUnitPos / 512];
 #pragma unroll
-      for (int u = 0; u < kUnitPos / 256; ++u) {
-        const int p = tl + 256 * u;
+      for (int u = 0; u < kUnitPos / 512; ++u) {
+        const int p = tl + 512 * u;
         pv[u] = col[start + min(p, count - 1)];
         sv[u] = slot[start + min(p, count - 1)];
       }
 #pragma unroll
-      for (int u = 0; u < kUnitPos / 256; ++u) {
-        const int p = tl + 256 * u;
+      for (int u = 0; u < kUnitPos / 512; ++u) {
+        const int p = tl + 512 * u;
         if (p < count) {
           sm.pos[p] = pv[u];
           sm.sl[p] = sv[u];
@@ -204,70 +216,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     }
     const int lane = tl & 63, h = lane >> 5, n = lane & 31;
-    const int kw = 32 * wave;  // this wave's keys kw .. kw+31; its d-slice for dQ
+    const int kq = wave & 3, dh = wave >> 2;
+    const int kw = 32 * kq;  // this wave's keys kw .. kw+31; its d-slice for dQ
     const int64_t key0 = (int64_t)b * kBlock;
-    // the wave's keys as the B operand of S and dP (d split by lane half)
-    bf16x8 kf[S], vf[S];
-    {
+    // Static operands in one register array, by role: producers hold the
+    // wave's keys as the B operand of S (fr[0..S)) and dP (fr[S..2S)), d
+    // split by lane half; consumers hold K^T of their d-slice over all 128
+    // keys as the A operand of dQ^T (fr[0..8)).
+    bf16x8 fr[2 * S];
+#pragma unroll
+    for (int s = 0; s < 2 * S; ++s) fr[s] = bf16x8{};
+    if (dh == 0) {
       const int64_t key = key0 + kw + n;
       const bool in = key < Nk;
       const int64_t off = ((in ? key : key0) * H_kv + r) * DH + (DH / 2) * h;
 #pragma unroll
       for (int s = 0; s < S; ++s) {
-        kf[s] = *reinterpret_cast<const bf16x8*>(K + off + 8 * s);
-        vf[s] = *reinterpret_cast<const bf16x8*>(V + off + 8 * s);
+        fr[s] = *reinterpret_cast<const bf16x8*>(K + off + 8 * s);
+        fr[S + s] = *reinterpret_cast<const bf16x8*>(V + off + 8 * s);
       }
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        kf[s] = in ? kf[s] : bf16x8{};
-        vf[s] = in ? vf[s] : bf16x8{};
-      }
-    }
-    // K^T of the wave's d-slice over all 128 keys, as the A operand of dQ^T
-    bf16x8 kT[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) kT[u] = bf16x8{};
-    if (kw < DH) {
+      for (int s = 0; s < 2 * S; ++s) fr[s] = in ? fr[s] : bf16x8{};
+    } else if (kw < DH) {
 #pragma unroll
       for (int u = 0; u < 8; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int64_t key = key0 + 16 * u + (e < 4 ? 4 * h + e : 8 + 4 * h + (e - 4));
-          const __bf16 x = K[((key < Nk ? key : key0) * H_kv + r) * DH + kw + n];
-          kT[u][e] = key < Nk ? x : f2bf(0.f);
+          const __bf16 xv = K[((key < Nk ? key : key0) * H_kv + r) * DH + kw + n];
+          fr[u][e] = key < Nk ? xv : f2bf(0.f);
         }
     }
     // every fragment load of the unit has landed before the tile loop, so no
     // wait inside the loop has to cover them
     __builtin_amdgcn_s_waitcnt(0);
 
-    // tile staging: thread -> (tensor, 4-row group, 16-byte chunk)
-    const int which = tl / (8 * CH);  // 0: Q, 1: dO, 2+: none (wave-uniform)
-    const int it = tl % (8 * CH), rq = it / CH, c = it % CH;
+    // tile staging: thread -> (tensor, 2-row group, 16-byte chunk)
+    const int which = tl / (16 * CH);  // 0: Q, 1: dO, 2+: none (wave-uniform)
+    const int it = tl % (16 * CH), rp = it / CH, c = it % CH;
     const int nrows = count * G;
     const int ntile = (nrows + 31) / 32;
     const int hq0 = r * G;
-    bf16x8 x[4];
+    bf16x8 x[2];
     int vmask = 0, mlim = -1;
     float ml2 = 0.f, mdv = 0.f;
+    // Every thread issues the same global loads (idle staging threads and
+    // rows past the end read a valid row), so the compiler can count the
+    // loads and stores in flight instead of waiting for all of them.
     auto load = [&](int T) {
       vmask = 0;
-      if (which < 2) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int R = 32 * T + 4 * rq + u;
-          const bool ok = R < nrows;
-          const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
-          const int64_t pos = sm.pos[pp];
-          const int hq = hq0 + (ok ? R - pp * G : 0);
-          const __bf16* src = which == 0 ? Q + (pos * H_q + hq) * DH
-                                         : dO + ((pos - q_start) * H_q + hq) * DH;
-          x[u] = *reinterpret_cast<const bf16x8*>(src + 8 * c);
-          vmask |= (int)ok << u;
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int R = 32 * T + 2 * rp + u;
+        const bool ok = which < 2 && R < nrows;
+        const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
+        const int64_t pos = sm.pos[pp];
+        const int hq = hq0 + (ok ? R - pp * G : 0);
+        const __bf16* src = which == 0 ? Q + (pos * H_q + hq) * DH
+                                       : dO + ((pos - q_start) * H_q + hq) * DH;
+        x[u] = *reinterpret_cast<const bf16x8*>(src + 8 * c);
+        vmask |= (int)ok << u;
       }
-      if (tl < 32) {
-        const int R = 32 * T + tl;
+      {
+        const int R = 32 * T + (tl & 31);
         const bool ok = R < nrows;
         const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
         const int64_t pos = sm.pos[pp];
@@ -278,28 +289,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         mlim = ok ? (int)(pos - key0) : -1;
       }
     };
-    auto store = [&](int bi) {
+    auto store = [&](int T) {
+      const int b2 = T & 1, b3 = T % 3;
       if (which < 2) {
-        __bf16* rm = which == 0 ? sm.qr[bi] : sm.gr[bi];
-        __bf16* tr = which == 0 ? sm.qt[bi] : sm.gt[bi];
-        bf16x8 y[4];
+        __bf16* rm = which == 0 ? sm.qr[b2] : sm.gr[b2];
+        __bf16* tr = which == 0 ? sm.qt[b3] : sm.gt[b3];
+        bf16x8 y[2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) y[u] = (vmask >> u) & 1 ? x[u] : bf16x8{};
+        for (int u = 0; u < 2; ++u) y[u] = (vmask >> u) & 1 ? x[u] : bf16x8{};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int row = 4 * rq + u;
+        for (int u = 0; u < 2; ++u) {
+          const int row = 2 * rp + u;
           *reinterpret_cast<bf16x8*>(&rm[row * DH + 8 * (c ^ row_swz<DH>(row))]) = y[u];
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<bf16x4*>(&tr[(8 * c + e) * kRp + 4 * rq]) =
-              bf16x4{y[0][e], y[1][e], y[2][e], y[3][e]};
+          *reinterpret_cast<bf16x2*>(&tr[(8 * c + e) * kRp + 2 * rp]) = bf16x2{y[0][e], y[1][e]};
       }
       if (tl < 32) {
-        sm.lim[bi][tl] = mlim;
-        sm.l2[bi][tl] = ml2 * kLog2e;
-        sm.dv[bi][tl] = mdv;
+        sm.lim[b2][tl] = mlim;
+        sm.l2[b2][tl] = ml2 * kLog2e;
+        sm.dv[b2][tl] = mdv;
       }
+    };
+    // consumer work on tile T (its producers' LDS output is complete): dV/dK
+    // of the second d-half, then dQ^T of the wave's d-slice stored as the
+    // rows' bf16 partials.  With T < 0 (nothing to consume) the MFMAs are
+    // skipped and zeros go to the spare slot, so the stores stay uniform.
+    f32x16 ak[NDH], av[NDH];
+    auto consume = [&](int T, int nn) {
+      const bool live = T >= 0;
+      const int b2 = T & 1, b3 = (T + 3) % 3;
+      f32x16 acc = {};
+      if (live) {
+#pragma unroll
+        for (int i = 0; i < NDH; ++i) {
+          const int dg = NDH + i;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            av[i] = mfma32(tr_frag<kRp>(sm.pt[b2], kw + nn, 16 * u, h),
+                           tr_frag<kRp>(sm.gt[b3], 32 * dg + nn, 16 * u, h), av[i]);
+            ak[i] = mfma32(tr_frag<kRp>(sm.dst[b2], kw + nn, 16 * u, h),
+                           tr_frag<kRp>(sm.qt[b3], 32 * dg + nn, 16 * u, h), ak[i]);
+          }
+        }
+        if (kw < DH) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            acc = mfma32(fr[u], tr_frag<kDsp>(sm.ds[b2], nn, 16 * u, h), acc);
+        }
+      }
+      const int R = 32 * T + n;
+      const bool ok = live && kw < DH && R < nrows;
+      const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
+      const int64_t ps = ok ? (sm.pos[pp] - q_start) * k + sm.sl[pp] : spare;
+      const int hl = ok ? R - pp * G : 0;
+      __bf16* dstp = part + (ps * H_kv + r) * (DH / 4) * G * 4 + hl * 4;
+      // accumulator rows are d = kw + 8qd + 4h + {0..3}: d-quad 8kq + 2qd + h
+      const int dq0 = ok ? 8 * kq : 0;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<bf16x4*>(dstp + (int64_t)(dq0 + 2 * qd + h) * G * 4) =
+            bf16x4{f2bf(acc[4 * qd]), f2bf(acc[4 * qd + 1]), f2bf(acc[4 * qd + 2]),
+                   f2bf(acc[4 * qd + 3])};
     };
 
     __syncthreads();  // positions staged
@@ -307,97 +359,97 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     store(0);
     if (ntile > 1) load(1);
     __syncthreads();
-    f32x16 ak[NDG], av[NDG];
 #pragma unroll
-    for (int dg = 0; dg < NDG; ++dg) ak[dg] = av[dg] = f32x16{};
+    for (int i = 0; i < NDH; ++i) ak[i] = av[i] = f32x16{};
     for (int T = 0; T < ntile; ++T) {
-      const int bi = T & 1;
+      const int b2 = T & 1, b3 = T % 3;
       // LDS indices go through an opaque copy of n so that the fragment
       // reads stay inside the loop rather than being hoisted into registers
       int nn = n;
       asm volatile("" : "+v"(nn));
-      // S = Q K^T and dP = dO V^T for the wave's 32 keys (key on the lane)
-      f32x16 sa = {}, pa = {};
+      if (dh == 0) {
+        // S = Q K^T and dP = dO V^T for the wave's 32 keys (key on the lane)
+        f32x16 sa = {}, pa = {};
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        sa = mfma32(rm_frag<DH>(sm.qr[bi], nn, s, h), kf[s], sa);
-        pa = mfma32(rm_frag<DH>(sm.gr[bi], nn, s, h), vf[s], pa);
-      }
-      bf16x8 pA[2], dA[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int row = acc_row(8 * u + e, h);
-          const int lm = sm.lim[bi][row];
-          const float l2 = sm.l2[bi][row], dv = sm.dv[bi][row];
-          const float ex = __builtin_amdgcn_exp2f(sa[8 * u + e] * scale_log2 - l2);
-          const float p = kw + n <= lm ? ex : 0.f;
-          pA[u][e] = f2bf(p);
-          dA[u][e] = f2bf(p * (pa[8 * u + e] - dv));
+        for (int s = 0; s < S; ++s) {
+          sa = mfma32(rm_frag<DH>(sm.qr[b2], nn, s, h), fr[s], sa);
+          pa = mfma32(rm_frag<DH>(sm.gr[b2], nn, s, h), fr[S + s], pa);
         }
-      // dV += P^T dO and dK += dS^T Q, contracting over the tile's rows
+        bf16x8 pA[2], dA[2];
 #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg)
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int row = acc_row(8 * u + e, h);
+            const int lm = sm.lim[b2][row];
+            const float l2 = sm.l2[b2][row], dv = sm.dv[b2][row];
+            const float ex = __builtin_amdgcn_exp2f(sa[8 * u + e] * scale_log2 - l2);
+            const float p = kw + n <= lm ? ex : 0.f;
+            pA[u][e] = f2bf(p);
+            dA[u][e] = f2bf(p * (pa[8 * u + e] - dv));
+          }
+        // dV += P^T dO and dK += dS^T Q over the tile's rows, first d-half
+#pragma unroll
+        for (int i = 0; i < NDH; ++i) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            av[i] = mfma32(pA[u], tr_frag<kRp>(sm.gt[b3], 32 * i + nn, 16 * u, h), av[i]);
+            ak[i] = mfma32(dA[u], tr_frag<kRp>(sm.qt[b3], 32 * i + nn, 16 * u, h), ak[i]);
+          }
+        }
+        // dS [row][key] for dQ; P^T and dS^T [key][row] for the consumers:
+        // registers 8u + 4q' .. +3 hold rows 16u + 8q' + 4h .. +3
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          av[dg] = mfma32(pA[u], tr_frag<kRp>(sm.gt[bi], 32 * dg + nn, 16 * u, h), av[dg]);
-          ak[dg] = mfma32(dA[u], tr_frag<kRp>(sm.qt[bi], 32 * dg + nn, 16 * u, h), ak[dg]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            sm.ds[b2][acc_row(8 * u + e, h) * kDsp + kw + nn] = dA[u][e];
+#pragma unroll
+          for (int qh = 0; qh < 2; ++qh) {
+            const int row0 = 16 * u + 8 * qh + 4 * h;
+            *reinterpret_cast<bf16x4*>(&sm.pt[b2][(kw + nn) * kRp + row0]) =
+                bf16x4{pA[u][4 * qh], pA[u][4 * qh + 1], pA[u][4 * qh + 2], pA[u][4 * qh + 3]};
+            *reinterpret_cast<bf16x4*>(&sm.dst[b2][(kw + nn) * kRp + row0]) =
+                bf16x4{dA[u][4 * qh], dA[u][4 * qh + 1], dA[u][4 * qh + 2], dA[u][4 * qh + 3]};
+          }
         }
-      // the wave's dS columns into the shared [row][key] tile
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sm.ds[bi][acc_row(8 * u + e, h) * kDsp + kw + nn] = dA[u][e];
-      // the next tile's rows into the other buffer, then fetch the one after
+        // producers store no dQ; the same (zero, spare-slot) stores as the
+        // consumers keep the memory counters uniform
+        consume(-1, nn);
+      } else {
+        consume(T - 1, nn);
+      }
+      (void)b3;
+      // the next tile's rows into the free buffers, then fetch the one after
       if (T + 1 < ntile) {
-        store(bi ^ 1);
+        store(T + 1);
         if (T + 2 < ntile) load(T + 2);
       }
       __syncthreads();
-      // dQ^T for the wave's d-slice = K^T dS^T over the block's 128 keys
-      if (kw < DH) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          acc = mfma32(kT[u], tr_frag<kDsp>(sm.ds[bi], nn, 16 * u, h), acc);
-        const int R = 32 * T + n;
-        const bool ok = R < nrows;
-        const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
-        const int64_t ps = ok ? (sm.pos[pp] - q_start) * k + sm.sl[pp] : spare;
-        const int hl = ok ? R - pp * G : 0;
-        __bf16* dst = part + (ps * H_kv + r) * (DH / 4) * G * 4 + hl * 4;
-        // accumulator rows are d = kw + 8qd + 4h + {0..3}: d-quad 8*wave + 2qd + h
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<bf16x4*>(dst + (int64_t)(8 * wave + 2 * qd + h) * G * 4) =
-              bf16x4{f2bf(acc[4 * qd]), f2bf(acc[4 * qd + 1]), f2bf(acc[4 * qd + 2]),
-                     f2bf(acc[4 * qd + 3])};
-      }
     }
+    if (dh == 1) consume(ntile - 1, n);
     // the unit's dK/dV sums: accumulator rows are keys, the lane is d
     if (pidx < 0) {
 #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg)
+      for (int i = 0; i < NDH; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int64_t key = key0 + kw + acc_row(j, h);
           if (key < Nk) {
-            const int64_t off = (key * H_kv + r) * DH + 32 * dg + n;
-            dK[off] += scale * ak[dg][j];
-            dV[off] += av[dg][j];
+            const int64_t off = (key * H_kv + r) * DH + 32 * (NDH * dh + i) + n;
+            dK[off] += scale * ak[i][j];
+            dV[off] += av[i][j];
           }
         }
     } else {
       float* pk = kvpart + (int64_t)pidx * 2 * kBlock * DH;
 #pragma unroll
-      for (int dg = 0; dg < NDG; ++dg)
+      for (int i = 0; i < NDH; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int kr = kw + acc_row(j, h);
-          pk[kr * DH + 32 * dg + n] = ak[dg][j];
-          pk[(kBlock + kr) * DH + 32 * dg + n] = av[dg][j];
+          const int kr = kw + acc_row(j, h), d = 32 * (NDH * dh + i) + n;
+          pk[kr * DH + d] = ak[i][j];
+          pk[(kBlock + kr) * DH + d] = av[i][j];
         }
     }
   }
@@ -528,7 +580,7 @@ hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const fl
   dim3 rgrid((unsigned)ceil_div(rows * (d_h / 4), (int64_t)256));
   dim3 sgrid((unsigned)std::min<int64_t>(bounds.max_splits, 2 * device_cus()));
   if (d_h == 128) {
-    bwd_fused_kernel<128><<<grid, 256, sizeof(BwdSmem<128>), stream>>>(
+    bwd_fused_kernel<128><<<grid, 512, sizeof(BwdSmem<128>), stream>>>(
         q, kk, v, g, lse, Dbuf, col, slot, units, n_units, q_start, Nk, H_q, H_kv, G, inv_G,
         nblk, k, spare, scale, scale_log2, part, kvpart, dK, dV);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -538,7 +590,7 @@ hipError_t launch_attn_bwd(const void* Q, const void* K, const void* V, const fl
     bwd_kv_reduce_kernel<128><<<sgrid, 256, 0, stream>>>(splits, n_splits, kvpart, H_kv, nblk,
                                                          Nk, scale, dK, dV);
   } else if (d_h == 64) {
-    bwd_fused_kernel<64><<<grid, 256, sizeof(BwdSmem<64>), stream>>>(
+    bwd_fused_kernel<64><<<grid, 512, sizeof(BwdSmem<64>), stream>>>(
         q, kk, v, g, lse, Dbuf, col, slot, units, n_units, q_start, Nk, H_q, H_kv, G, inv_G,
         nblk, k, spare, scale, scale_log2, part, kvpart, dK, dV);
     if ((e = hipGetLastError()) != hipSuccess) return e;
