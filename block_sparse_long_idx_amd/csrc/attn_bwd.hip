@@ -456,30 +456,34 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
 }
 
 // dQ[i, h] = scale * sum over the row's slots (ascending) of the partials.
+// Thread -> (row i, group r, d-quad, head in group), head fastest: a
+// partial row group [d_h/4][G][4] is then read contiguously by consecutive
+// threads, and each head's dQ row gets whole 64-byte runs.
 template <int DH>
 __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const __bf16* __restrict__ part,
                                                             int64_t q_start, int64_t Nq,
                                                             int H_q, int H_kv, int k,
                                                             float scale, float* __restrict__ dQ) {
-  // one thread per (iq, h, d-quad)
   const int G = H_q / H_kv;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= Nq * H_q * (DH / 4)) return;
-  const int dq = (int)(gid % (DH / 4));
-  const int64_t ih = gid / (DH / 4);
-  const int h = (int)(ih % H_q);
-  const int64_t iq = ih / H_q;
-  const int r = h / G;
+  const int hl = (int)(gid % G);
+  const int64_t rest = gid / G;
+  const int dq = (int)(rest % (DH / 4));
+  const int64_t ir = rest / (DH / 4);
+  const int r = (int)(ir % H_kv);
+  const int64_t iq = ir / H_kv;
   const int n_sel = (int)min((int64_t)k, (q_start + iq) / kBlock + 1);
+  const __bf16* src = part + ((iq * k) * H_kv + r) * (DH / 4) * G * 4 + ((int64_t)dq * G + hl) * 4;
+  const int64_t slot_stride = (int64_t)H_kv * (DH / 4) * G * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < n_sel; ++s) {
-    const bf16x4 x = *reinterpret_cast<const bf16x4*>(
-        part + ((iq * k + s) * H_kv + r) * (DH / 4) * G * 4 + (int64_t)dq * G * 4 + (h - r * G) * 4);
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(src + s * slot_stride);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += bf2f(x[e]);
   }
   // d-quad dq holds d = 4*dq .. 4*dq+3
-  *reinterpret_cast<f32x4*>(dQ + (iq * H_q + h) * DH + 4 * dq) =
+  *reinterpret_cast<f32x4*>(dQ + (iq * H_q + r * G + hl) * DH + 4 * dq) =
       f32x4{acc[0] * scale, acc[1] * scale, acc[2] * scale, acc[3] * scale};
 }
 
