@@ -56,6 +56,9 @@ def _load():
         lib.oracle_attend.restype = None
         lib.oracle_invert.argtypes = [P, i64, i64, i32, i32, i64, P, P, P]
         lib.oracle_invert.restype = i64
+        lib.oracle_attend_backward_dq_rows.argtypes = [P, P, P, P, P, P, i64, i32, i32, i32,
+                                                       i32, i32, f64, P, i32]
+        lib.oracle_attend_backward_dq_rows.restype = None
         lib.oracle_decode_one.argtypes = [P, P, P, P, P, i64, i32, i32, i32,
                                           i32, i32, i32, f64, P, P, P, i32]
         lib.oracle_decode_one.restype = None
@@ -199,6 +202,28 @@ def attend_backward(Q, K, V, dO, sel, scale, B_k=128, nthreads=None):
                                    H_kv, d_h, B_k, k, float(scale), _ptr(dQ), _ptr(dK),
                                    _ptr(dV), nthreads or threads())
     return dQ, dK, dV
+
+
+def attend_backward_dq_rows(Q_rows, K, V, dO_rows, sel_rows, rows, scale, B_k=128,
+                            nthreads=None):
+    """dQ of the given query rows only (no dK/dV), fp64.
+
+    Q_rows, dO_rows: uint16 [R, H_q, d_h]; K, V: uint16 [Nk, H_kv, d_h];
+    sel_rows: int32 [R, H_kv, k]; rows: their positions.
+    """
+    Q_rows, K, V, dO_rows = _u16(Q_rows), _u16(K), _u16(V), _u16(dO_rows)
+    sel_rows = np.ascontiguousarray(sel_rows, dtype=np.int32)
+    pos = np.ascontiguousarray(rows, dtype=np.int64)
+    R, H_q, d_h = Q_rows.shape
+    H_kv = K.shape[1]
+    k = sel_rows.shape[2]
+    assert dO_rows.shape == Q_rows.shape and sel_rows.shape == (R, H_kv, k) and pos.shape == (R,)
+    assert pos.max() < K.shape[0]
+    dQ = np.empty((R, H_q, d_h), dtype=np.float64)
+    _load().oracle_attend_backward_dq_rows(_ptr(Q_rows), _ptr(K), _ptr(V), _ptr(dO_rows),
+                                           _ptr(sel_rows), _ptr(pos), R, H_q, H_kv, d_h, B_k,
+                                           k, float(scale), _ptr(dQ), nthreads or threads())
+    return dQ
 
 
 def decode_one(q, q_idx, K, V, k_idx, k, scale, B_k=128, nthreads=None):

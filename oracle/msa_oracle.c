@@ -427,10 +427,11 @@ void oracle_index_kl(const uint16_t *q_rows, const uint16_t *k_idx, const uint16
 typedef struct {
     const uint16_t *Q, *K, *V, *dO;
     const int32_t *sel;
-    int64_t N;
+    int64_t N;              /* rows of Q, dO, sel, dQ */
+    const int64_t *pos;     /* their positions (NULL: row i is position i) */
     int H_q, H_kv, d_h, B_k, k;
     double scale;
-    double *dQ, *dK, *dV;   /* dK, dV: this thread's private accumulators */
+    double *dQ, *dK, *dV;   /* dK, dV: this thread's private accumulators (NULL: dQ only) */
     int tid, nthreads;
 } bwd_job_t;
 
@@ -443,11 +444,12 @@ static void *run_bwd(void *arg)
     double *p = (double *)malloc(sizeof(double) * (size_t)cap);
     double *O = (double *)malloc(sizeof(double) * (size_t)d_h);
     for (int64_t u = jb->tid; u < jb->N * jb->H_q; u += jb->nthreads) {
-        const int64_t i = u / jb->H_q;
+        const int64_t ii = u / jb->H_q;                 /* row of the inputs */
+        const int64_t i = jb->pos ? jb->pos[ii] : ii;   /* its position */
         const int h = (int)(u % jb->H_q), r = h / G;
-        const uint16_t *q = jb->Q + (i * jb->H_q + h) * d_h;
-        const uint16_t *go = jb->dO + (i * jb->H_q + h) * d_h;
-        const int32_t *srow = jb->sel + (i * jb->H_kv + r) * jb->k;
+        const uint16_t *q = jb->Q + (ii * jb->H_q + h) * d_h;
+        const uint16_t *go = jb->dO + (ii * jb->H_q + h) * d_h;
+        const int32_t *srow = jb->sel + (ii * jb->H_kv + r) * jb->k;
         int64_t n = 0;
         for (int t = 0; t < jb->k; ++t) {
             if (srow[t] < 0)
@@ -479,7 +481,7 @@ static void *run_bwd(void *arg)
         double Dv = 0.0;
         for (int d = 0; d < d_h; ++d)
             Dv += widen_bf16(go[d]) * O[d];
-        double *dq = jb->dQ + (i * jb->H_q + h) * d_h;
+        double *dq = jb->dQ + (ii * jb->H_q + h) * d_h;
         for (int d = 0; d < d_h; ++d)
             dq[d] = 0.0;
         for (int64_t a = 0; a < n; ++a) {
@@ -488,10 +490,13 @@ static void *run_bwd(void *arg)
             for (int d = 0; d < d_h; ++d)
                 dp += widen_bf16(go[d]) * widen_bf16(jb->V[base + d]);
             const double ds = p[a] * (dp - Dv);
-            for (int d = 0; d < d_h; ++d) {
+            for (int d = 0; d < d_h; ++d)
                 dq[d] += jb->scale * ds * widen_bf16(jb->K[base + d]);
-                jb->dK[base + d] += jb->scale * ds * widen_bf16(q[d]);
-                jb->dV[base + d] += p[a] * widen_bf16(go[d]);
+            if (jb->dK) {
+                for (int d = 0; d < d_h; ++d) {
+                    jb->dK[base + d] += jb->scale * ds * widen_bf16(q[d]);
+                    jb->dV[base + d] += p[a] * widen_bf16(go[d]);
+                }
             }
         }
     }
@@ -514,7 +519,8 @@ void oracle_attend_backward(const uint16_t *Q, const uint16_t *K, const uint16_t
     for (int t = 0; t < nthreads; ++t) {
         bwd_job_t *jb = &jobs[t];
         jb->Q = Q; jb->K = K; jb->V = V; jb->dO = dO; jb->sel = sel;
-        jb->N = N; jb->H_q = H_q; jb->H_kv = H_kv; jb->d_h = d_h; jb->B_k = B_k; jb->k = k;
+        jb->N = N; jb->pos = NULL;
+        jb->H_q = H_q; jb->H_kv = H_kv; jb->d_h = d_h; jb->B_k = B_k; jb->k = k;
         jb->scale = scale; jb->dQ = dQ;
         jb->dK = (double *)calloc(kv, sizeof(double));
         jb->dV = (double *)calloc(kv, sizeof(double));
@@ -533,6 +539,39 @@ void oracle_attend_backward(const uint16_t *Q, const uint16_t *K, const uint16_t
         free(jobs[t].dK);
         free(jobs[t].dV);
     }
+    free(th);
+    free(jobs);
+}
+
+/*
+ * dQ alone for chosen query rows: the same per-row computation as
+ * oracle_attend_backward, for rows at positions pos[0..n_rows) (their Q,
+ * dO and selection rows given compactly), without the dK/dV sums.
+ *   Q_rows, dO_rows: [n_rows, H_q, d_h]; sel_rows: [n_rows, H_kv, k]
+ *   K, V: [>= max(pos)+1, H_kv, d_h]; dQ_rows out [n_rows, H_q, d_h]
+ */
+void oracle_attend_backward_dq_rows(const uint16_t *Q_rows, const uint16_t *K,
+                                    const uint16_t *V, const uint16_t *dO_rows,
+                                    const int32_t *sel_rows, const int64_t *pos, int64_t n_rows,
+                                    int H_q, int H_kv, int d_h, int B_k, int k, double scale,
+                                    double *dQ_rows, int nthreads)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    bwd_job_t *jobs = (bwd_job_t *)malloc(sizeof(bwd_job_t) * (size_t)nthreads);
+    for (int t = 0; t < nthreads; ++t) {
+        bwd_job_t *jb = &jobs[t];
+        jb->Q = Q_rows; jb->K = K; jb->V = V; jb->dO = dO_rows; jb->sel = sel_rows;
+        jb->N = n_rows; jb->pos = pos;
+        jb->H_q = H_q; jb->H_kv = H_kv; jb->d_h = d_h; jb->B_k = B_k; jb->k = k;
+        jb->scale = scale; jb->dQ = dQ_rows; jb->dK = NULL; jb->dV = NULL;
+        jb->tid = t;
+        jb->nthreads = nthreads;
+        pthread_create(&th[t], NULL, run_bwd, jb);
+    }
+    for (int t = 0; t < nthreads; ++t)
+        pthread_join(th[t], NULL);
     free(th);
     free(jobs);
 }

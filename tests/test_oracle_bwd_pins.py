@@ -103,3 +103,17 @@ def test_backward_exact_sums(oracle_lib):
         np.testing.assert_allclose(dV[:, r, :].sum(0), dO[:, r * G:(r + 1) * G, :].sum((0, 1)),
                                    rtol=0, atol=1e-9)
         np.testing.assert_allclose(dK[:, r, :].sum(0), 0.0, atol=1e-9)
+
+
+def test_backward_dq_rows_matches_torch_on_sampled_rows(oracle_lib):
+    """The rows-only dQ entry point (used where only sampled rows can be
+    checked) against torch autograd on those rows."""
+    N, H_q, H_kv, d_h, k = 800, 6, 2, 32, 3
+    t, u = _inputs(N, H_q, H_kv, d_h, 16, seed=47, n_hot=2)
+    rows = np.array([0, 5, 127, 128, 300, 511, 640, 799])
+    sel = oracle_lib.select(u["q_idx"], u["k_idx"], np.arange(N), k)
+    scale = 1 / math.sqrt(d_h)
+    dq = oracle_lib.attend_backward_dq_rows(u["Q"][rows], u["K"], u["V"], u["dO"][rows],
+                                            sel[rows], rows, scale)
+    tQ, _, _ = _torch_grads(t, _mask_from_sel(sel, N), scale)
+    np.testing.assert_allclose(dq, tQ[rows], rtol=0, atol=1e-10)
