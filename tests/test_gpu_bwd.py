@@ -99,3 +99,89 @@ def test_attn_bwd_deterministic():
     torch.cuda.synchronize()
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_attn_bwd_8k_group0(oracle_lib):
+    """The 8K workload's full shape (64 query heads, 4 groups, d_h 128,
+    k 16) through the GPU backward; groups are independent, so group 0 is
+    checked against the oracle run on that group alone."""
+    from block_sparse_long_idx_amd.synth import CONFIGS, inputs_for, make_grad_output
+    cfg = CONFIGS["8k"]
+    say("attn_bwd 8k group 0")
+    t = inputs_for(cfg)
+    dO = make_grad_output(cfg.N, cfg.H_q, cfg.d_h, seed=cfg.seed + 17)
+    u = {key: bf16_bits(v) for key, v in t.items()}
+    rows = np.arange(cfg.N)
+    sel = oracle_lib.select(u["q_idx"], u["k_idx"], rows, cfg.k)
+    rp, col, slot = oracle_lib.invert(sel, 0, cfg.nblk)
+    d = {key: v.cuda() for key, v in t.items()}
+    rp_d = torch.from_numpy(rp.astype(np.int32)).cuda()
+    col_d = torch.from_numpy(col.astype(np.int32)).cuda()
+    slot_d = torch.from_numpy(slot.astype(np.uint8)).cuda()
+    O, lse = msa.sparse_attn_fwd(d["Q"], d["K"], d["V"], rp_d, col_d, slot_d, cfg.k,
+                                 scale=cfg.scale)
+    dQ, dK, dV = msa.sparse_attn_bwd(d["Q"], d["K"], d["V"], O, lse, dO.cuda(), rp_d, col_d,
+                                     slot_d, cfg.k, scale=cfg.scale)
+    torch.cuda.synchronize()
+    G = cfg.H_q // cfg.H_kv
+    dQ_ref, dK_ref, dV_ref = oracle_lib.attend_backward(
+        np.ascontiguousarray(u["Q"][:, :G]), np.ascontiguousarray(u["K"][:, :1]),
+        np.ascontiguousarray(u["V"][:, :1]), np.ascontiguousarray(bf16_bits(dO)[:, :G]),
+        np.ascontiguousarray(sel[:, :1]), cfg.scale)
+    assert_grad_close("dQ", dQ[:, :G].cpu().numpy(), dQ_ref)
+    assert_grad_close("dK", dK[:, :1].cpu().numpy(), dK_ref)
+    assert_grad_close("dV", dV[:, :1].cpu().numpy(), dV_ref)
+
+
+@pytest.mark.slow
+def test_attn_bwd_1m_sampled(oracle_lib):
+    """The 1M workload's backward in the benchmark's launch shape (16 query
+    chunks of 65,536, dK/dV accumulated across them) after the GPU forward:
+    dQ on sampled rows against the oracle, and the exact identity
+    sum_j dV[j, r] = sum of dO over group r's (row, head) pairs."""
+    from block_sparse_long_idx_amd.synth import CONFIGS, inputs_for, make_grad_output, sample_rows
+    cfg = CONFIGS["1m"]
+    say("attn_bwd 1m sampled")
+    t = inputs_for(cfg, device="cuda")
+    dO = make_grad_output(cfg.N, cfg.H_q, cfg.d_h, seed=cfg.seed + 17, device="cuda")
+    sel = msa.index_topk(t["q_idx"], t["k_idx"], cfg.k)
+    O = torch.empty((cfg.N, cfg.H_q, cfg.d_h), dtype=torch.float32, device="cuda")
+    lse = torch.empty((cfg.N, cfg.H_q), dtype=torch.float32, device="cuda")
+    dQ = torch.empty_like(O)
+    dK = torch.zeros((cfg.N, cfg.H_kv, cfg.d_h), dtype=torch.float32, device="cuda")
+    dV = torch.zeros_like(dK)
+    for q0 in range(0, cfg.N, cfg.chunk):
+        rp, col, slot = msa.invert_index(sel[q0:q0 + cfg.chunk], q_start=q0)
+        msa.sparse_attn_fwd(t["Q"], t["K"], t["V"], rp, col, slot, cfg.k, q_start=q0,
+                            Nq=cfg.chunk, scale=cfg.scale, O=O[q0:q0 + cfg.chunk],
+                            lse=lse[q0:q0 + cfg.chunk])
+        msa.sparse_attn_bwd(t["Q"], t["K"], t["V"], O[q0:q0 + cfg.chunk],
+                            lse[q0:q0 + cfg.chunk], dO[q0:q0 + cfg.chunk], rp, col, slot,
+                            cfg.k, q_start=q0, Nq=cfg.chunk, scale=cfg.scale,
+                            dQ=dQ[q0:q0 + cfg.chunk], dK=dK, dV=dV)
+        del rp, col, slot
+    torch.cuda.synchronize()
+    rows = np.array(sample_rows(cfg.N, 48))
+    rt = torch.from_numpy(rows).cuda()
+    u = {key: bf16_bits(t[key][rt]) for key in ("Q", "q_idx")}
+    K, V, kx = bf16_bits(t["K"]), bf16_bits(t["V"]), bf16_bits(t["k_idx"])
+    sel_ref = oracle_lib.select(u["q_idx"], kx, rows, cfg.k)
+    np.testing.assert_array_equal(sel[rt].cpu().numpy(), sel_ref)
+    dq_ref = oracle_lib.attend_backward_dq_rows(u["Q"], K, V, bf16_bits(dO[rt]), sel_ref, rows,
+                                                cfg.scale)
+    assert_grad_close("dQ (sampled rows)", dQ[rt].cpu().numpy(), dq_ref)
+    # sum_j p_j = 1 for every (row, head): the dV column sums are the dO sums
+    G = cfg.H_q // cfg.H_kv
+    got = dV.double().sum(0)                                     # [H_kv, d_h]
+    want = torch.zeros((cfg.H_kv, cfg.d_h), dtype=torch.float64, device="cuda")
+    scale_ref = torch.zeros_like(want)
+    for q0 in range(0, cfg.N, cfg.chunk):                        # bounded temporaries
+        g = dO[q0:q0 + cfg.chunk].double().view(-1, cfg.H_kv, G, cfg.d_h)
+        want += g.sum((0, 2))
+        scale_ref += g.abs().sum((0, 2))
+        del g
+    err = ((got - want).abs() / scale_ref).max().item()
+    print(f"[bwd] 1M dV column sums: max |err| / sum|dO| = {err:.2e}", flush=True)
+    # bf16 P perturbs each row's sum of p by ~2^-9 with random sign; over
+    # 2^24 (row, head) pairs that averages to ~1e-6 of sum|dO| at most
+    assert err <= 1e-5, err
