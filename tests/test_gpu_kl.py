@@ -105,3 +105,33 @@ def test_index_kl_end_to_end_8k(oracle_lib):
     kl_ref = oracle_lib.index_kl(u["q_idx"][rows], u["k_idx"], u["Q"][rows], u["K"], sel_ref,
                                  rows, cfg.scale)
     assert_kl_close(kl.cpu().numpy()[rows], kl_ref, cfg.d_idx)
+
+
+@pytest.mark.slow
+def test_index_kl_1m_sampled(oracle_lib):
+    """The 1M workload's KL pass over every chunk, after the GPU selection
+    and forward, checked on sampled rows (each (row, group) value depends on
+    that row alone)."""
+    from block_sparse_long_idx_amd.synth import sample_rows
+    cfg = CONFIGS["1m"]
+    say("index_kl 1m sampled")
+    t = inputs_for(cfg, device="cuda")
+    sel = msa.index_topk(t["q_idx"], t["k_idx"], cfg.k)
+    kl = torch.empty((cfg.N, cfg.H_kv), dtype=torch.float32, device="cuda")
+    for q0 in range(0, cfg.N, cfg.chunk):
+        rp, col, slot = msa.invert_index(sel[q0:q0 + cfg.chunk], q_start=q0)
+        _, lse = msa.sparse_attn_fwd(t["Q"], t["K"], t["V"], rp, col, slot, cfg.k, q_start=q0,
+                                     Nq=cfg.chunk, scale=cfg.scale)
+        msa.index_kl(t["Q"], t["K"], t["q_idx"], t["k_idx"], lse, rp, col, slot, cfg.k,
+                     q_start=q0, Nq=cfg.chunk, scale=cfg.scale, want_sum=False,
+                     kl=kl[q0:q0 + cfg.chunk])
+        del rp, col, slot, lse
+    torch.cuda.synchronize()
+    rows = np.array(sample_rows(cfg.N, 64))
+    rt = torch.from_numpy(rows).cuda()
+    u = {key: bf16_bits(t[key][rt]) for key in ("Q", "q_idx")}
+    K, kx = bf16_bits(t["K"]), bf16_bits(t["k_idx"])
+    sel_ref = oracle_lib.select(u["q_idx"], kx, rows, cfg.k)
+    np.testing.assert_array_equal(sel[rt].cpu().numpy(), sel_ref)
+    kl_ref = oracle_lib.index_kl(u["q_idx"], kx, u["Q"], K, sel_ref, rows, cfg.scale)
+    assert_kl_close(kl[rt].cpu().numpy(), kl_ref, cfg.d_idx)

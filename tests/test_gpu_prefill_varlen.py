@@ -21,6 +21,16 @@ pytestmark = pytest.mark.gpu
 ATOL, RTOL_L2, LSE_ATOL = 1e-2, 5e-3, 1e-3
 
 
+@pytest.fixture(params=[0, 1], ids=["twokernel", "fused"])
+def index_variant(request):
+    """Both Index Branch variants: per-chunk score GEMM + Top-k kernel, and
+    the fused kernel (run once over each span)."""
+    old = msa.get_option(msa.OPT_INDEX_FUSED)
+    msa.set_option(msa.OPT_INDEX_FUSED, request.param)
+    yield request.param
+    msa.set_option(msa.OPT_INDEX_FUSED, old)
+
+
 def say(*a):
     print("[case]", *a, flush=True)
     sys.stdout.flush()
@@ -38,7 +48,7 @@ def assert_attn_close(O, O_ref, lse, lse_ref):
 
 @pytest.mark.parametrize("splits,inner", [((1000, 2100, 3000), 0), ((1, 700, 3000), 512),
                                           ((2999, 3000), 0)])
-def test_prefill_cached(oracle_lib, splits, inner):
+def test_prefill_cached(oracle_lib, splits, inner, index_variant):
     """A 3000-token sequence arriving in pieces; each piece is attended with
     only its own Q/q_idx rows and a cache holding exactly the keys so far."""
     N, H_q, H_kv, d_h, d_idx, k = 3000, 16, 4, 64, 64, 6
@@ -66,7 +76,7 @@ def test_prefill_cached(oracle_lib, splits, inner):
 
 @pytest.mark.parametrize("lens,inner", [((1000, 129, 1, 2600, 0, 777), 0),
                                         ((300, 2048, 513), 1024)])
-def test_prefill_varlen(oracle_lib, lens, inner):
+def test_prefill_varlen(oracle_lib, lens, inner, index_variant):
     """Independently generated sequences packed back to back: each one's
     rows must equal the oracle on that sequence alone."""
     H_q, H_kv, d_h, d_idx, k = 8, 2, 128, 32, 5
