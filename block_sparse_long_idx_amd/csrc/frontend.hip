@@ -9,8 +9,8 @@
 // their form; these are the plain readings (rotate-half pairing).
 //
 // One MFMA GEMM per projection with the norm and rotation in its epilogue:
-// a work-group computes 128 rows x 256 output columns (four waves, 64 x 128
-// each), staging 64-wide slabs of the contraction in LDS by direct
+// a work-group computes 256 rows x 256 output columns (eight waves, 64 x
+// 128 each, two per SIMD), staging 64-wide slabs of the contraction in LDS by direct
 // global->LDS loads (two buffers, 16-byte chunks XOR-swizzled by row).  The
 // q and k work-groups of one row tile run on the same XCD, so the second
 // read of those hidden rows hits that XCD's L2.  Angles are reduced to a
@@ -25,7 +25,8 @@ namespace msa {
 
 namespace {
 
-constexpr int FM = 128, FN = 256, FK = 64;
+constexpr int NWR = 4;                    // waves along the rows (x 2 along the columns)
+constexpr int FM = 64 * NWR, FN = 256, FK = 64;
 
 struct FeSmem {
   __bf16 a[2][FM * FK];  // hidden rows [row][64]
@@ -40,9 +41,9 @@ __device__ __forceinline__ bf16x8 fe_frag(const __bf16* t, int row, int s, int h
 
 }  // namespace
 
-// 96 KiB of LDS: one work-group per CU, so one wave per SIMD.
+// 128 KiB of LDS: one work-group of eight waves per CU, two per SIMD.
 template <int DI, int R>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void index_frontend_kernel(
+__global__ __launch_bounds__(128 * NWR) void index_frontend_kernel(
     const __bf16* __restrict__ X, const __bf16* __restrict__ Wq, const __bf16* __restrict__ Wk,
     const float* __restrict__ gq, const float* __restrict__ gk, __bf16* __restrict__ oq,
     __bf16* __restrict__ ok, int64_t N, int64_t pos0, int d_model, int ncols, int n_rt,
@@ -63,22 +64,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int64_t row0 = (int64_t)rt * FM;
   const int col0 = blockIdx.y * FN;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, h = lane >> 5, n = lane & 31;
-  const int wr = wave & 1, wc = wave >> 1;
+  const int wr = wave % NWR, wc = wave / NWR;
 
   // Each wave instruction fills 1 KiB = 8 rows of 64; lane i writes chunk
   // position i % 8 of row i / 8, so it fetches the chunk that lands there.
   auto dma = [&](int kk, int buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int v = wave * 4 + q;
+    for (int q = 0; q < FM / 8 / (2 * NWR); ++q) {
+      const int v = wave * (FM / 8 / (2 * NWR)) + q;
       const int rr = 8 * v + (lane >> 3), p = lane & 7;
       const int64_t grow = min(row0 + rr, N - 1);
       const __bf16* src = X + grow * d_model + (int64_t)kk * FK + 8 * (p ^ (rr & 7));
       __builtin_amdgcn_global_load_lds(src, &sm.a[buf][v * 512], 16, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int v = wave * 8 + q;
+    for (int q = 0; q < FN / 8 / (2 * NWR); ++q) {
+      const int v = wave * (FN / 8 / (2 * NWR)) + q;
       const int rr = 8 * v + (lane >> 3), p = lane & 7;
       const int64_t gcol = min(col0 + rr, ncols - 1);
       const __bf16* src = W + gcol * d_model + (int64_t)kk * FK + 8 * (p ^ (rr & 7));
@@ -221,7 +222,7 @@ hipError_t launch_index_frontend(const void* hidden, const void* Wq, const void*
   auto* ok = static_cast<__bf16*>(k_idx);
   const size_t lds = sizeof(FeSmem);
 #define MSA_FE(DI, R)                                                                      \
-  index_frontend_kernel<DI, R><<<grid, 256, lds, stream>>>(x, wq, wk, gq, gk, oq, ok, N,  \
+  index_frontend_kernel<DI, R><<<grid, 128 * NWR, lds, stream>>>(x, wq, wk, gq, gk, oq, ok, N,  \
                                                            pos0, d_model, ncols, n_rt,    \
                                                            log2_theta, eps)
   if (d_idx == 32 && rope_dim == 0) MSA_FE(32, 0);
