@@ -147,10 +147,12 @@ msa_status msa_prefill(const void *Q, const void *K, const void *V,
                        float *lse, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Chunked prefill against a KV cache: the Nq new tokens at positions
- * q_start .. q_start+Nq-1 attend causally to the cached tokens and to each
- * other, exactly as rows q_start.. of msa_prefill over the whole sequence
- * (each row depends only on its own prefix).
+ * Chunked prefill against a KV cache (section 02: each query row's
+ * selection and attention range over its own causal prefix only, so a
+ * sequence can be prefilled piece by piece against the keys already
+ * cached): the Nq new tokens at positions q_start .. q_start+Nq-1 attend
+ * causally to the cached tokens and to each other, exactly as rows
+ * q_start.. of msa_prefill over the whole sequence.
  *   Q [Nq, H_q, d_h], q_idx [Nq, H_kv, d_idx]: the new tokens only
  *   K, V [q_start+Nq, H_kv, d_h], k_idx [q_start+Nq, H_kv, d_idx]: the
  *     cache with the new tokens' keys already appended
@@ -169,7 +171,9 @@ msa_status msa_prefill_cached(const void *Q, const void *K, const void *V,
                               void *stream);
 
 /*
- * Varlen batched prefill: B independent sequences packed token-major.
+ * Varlen batched prefill (section 02, as above: sequences share nothing,
+ * so each is its own causal prefill): B independent sequences packed
+ * token-major.
  * Sequence b is rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of every tensor,
  * with its own positions 0..L_b-1 and its own causal prefix; it gets the
  * msa_prefill result of that sequence alone.  Sequences run one after
