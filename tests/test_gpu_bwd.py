@@ -43,6 +43,7 @@ BWD_CASES = [
     (2600, 6, 2, 128, 32, 16, 4, 1000),   # G = 3, k = 16, chunks not on block edges
     (777, 2, 2, 64, 32, 1, 0, 0),         # k = 1: local block only
     (600, 64, 1, 128, 64, 3, 1, 0),       # G = 64
+    (4500, 4, 4, 128, 64, 32, 3, 1500),   # G = 1, k = 32 (rows past 4096 fill every slot)
 ]
 
 
