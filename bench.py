@@ -251,12 +251,12 @@ def time_bwd(pf, cfg, t, reps=2):
     ms = total_ms / reps
     G = cfg.H_q // cfg.H_kv
     d = cfg.d_h
-    # per (query, head, selected block): the dQ pass reads Q, dO, lse, delta
-    # and writes a bf16 dQ partial; the dK/dV pass reads Q, dO, lse, delta
-    # again; the reduce reads the partial back.  Per (query, head): delta
-    # reads O (fp32) and dO, the reduce writes dQ (fp32).
+    # per (query, head, selected block): the fused pass reads Q, dO, lse and
+    # delta once and writes a bf16 dQ partial, which the reduce reads back.
+    # Per (query, head): delta reads O (fp32) and dO and writes delta; the
+    # reduce writes dQ (fp32).
     pairs = nnz * G
-    nbytes = pairs * (12 * d + 16) + cfg.N * cfg.H_q * (6 * d + 4 * d + 4)
+    nbytes = pairs * (8 * d + 8) + cfg.N * cfg.H_q * (6 * d + 4 * d + 4)
     flops = 10.0 * cfg.H_q * d * cfg.N * cfg.k * cfg.B_k
     ok = bool(torch.isfinite(dQ).all().item() and torch.isfinite(dK).all().item()
               and torch.isfinite(dV).all().item())
