@@ -249,7 +249,10 @@ def test_full_128k(oracle_lib, index_variant):
 
 
 @pytest.mark.slow
-def test_full_1m(oracle_lib):
+def test_full_1m(oracle_lib, index_variant):
+    """The fused variant is the configuration the benchmark times: one
+    Index Branch launch over all 1,048,576 queries, then the inverted index
+    and the Main Branch per 65,536-query chunk."""
     _full_prefill_check(oracle_lib, CONFIGS["1m"], 256)
 
 
