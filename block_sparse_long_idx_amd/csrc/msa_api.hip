@@ -14,7 +14,7 @@
 namespace {
 
 thread_local std::string g_err;
-int64_t g_opt_fused = 0;
+int64_t g_opt_fused = 1;
 int64_t g_opt_chunk = 1024;
 
 constexpr int kB = 128;

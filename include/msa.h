@@ -300,9 +300,11 @@ msa_status msa_index_frontend(const void *hidden, const void *Wq, const void *Wk
 
 /*
  * Tuning knobs (process-wide; they change speed, never results).
- *   MSA_OPT_INDEX_FUSED: 1 = Index Branch as one kernel that keeps a
- *     running Top-k per query next to the score GEMM; 0 = GEMM writes the
- *     block scores, a separate wavefront-per-row Top-k reads them.
+ *   MSA_OPT_INDEX_FUSED: 1 (default) = Index Branch as one kernel that
+ *     keeps a running Top-k per query next to the score GEMM (it uses no
+ *     workspace, and msa_prefill runs it once over the whole sequence when
+ *     the caller passes sel); 0 = GEMM writes the block scores, a separate
+ *     wavefront-per-row Top-k reads them.  Both give identical sel.
  *   MSA_OPT_ATTN_CHUNK: max query positions per KV-outer work item, 1..2048
  *     (section 05 part 2: hot blocks are cut along the query dimension).
  * Returns MSA_ERR_INVALID_ARG for an unknown option or value.

@@ -62,8 +62,19 @@ def _err(lib):
      msa.ERR_UNSUPPORTED),   # more than 16384 blocks
 ])
 def test_index_topk_rejects(lib, args, status):
-    assert lib.msa_index_topk(*args, NULL) == status
-    assert _err(lib)
+    # the two-kernel variant, which alone needs the score workspace; every
+    # other check is the same for both
+    old = msa.get_option(msa.OPT_INDEX_FUSED)
+    msa.set_option(msa.OPT_INDEX_FUSED, 0)
+    try:
+        assert lib.msa_index_topk(*args, NULL) == status
+        assert _err(lib)
+    finally:
+        msa.set_option(msa.OPT_INDEX_FUSED, old)
+
+
+def test_index_fused_is_default(lib):
+    assert msa.get_option(msa.OPT_INDEX_FUSED) == 1
 
 
 def test_invert_rejects(lib):
