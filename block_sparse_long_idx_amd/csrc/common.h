@@ -49,19 +49,42 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
   return x;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int o) {
-  uint32_t lo = __shfl_xor((uint32_t)x, o, kWave);
-  uint32_t hi = __shfl_xor((uint32_t)(x >> 32), o, kWave);
+__device__ __forceinline__ uint64_t join_u64(uint32_t lo, uint32_t hi) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// max(x, x of the lane that the DPP control CTRL maps onto this one)
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t x) {
+  const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
+  const uint64_t y = join_u64((uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false),
+                              (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false));
+  return y > x ? y : x;
+}
+
+// Maximum over the 64 lanes, returned wave-uniform, without LDS traffic:
+// DPP quad_perm pairs lanes 1 and then 2 apart (every lane then holds its
+// quad's maximum), row_half_mirror pairs the two quads of each 8-lane
+// group, row_mirror the two 8-lane groups of each 16-lane row, ds_swizzle
+// (bit mode, xor 16) the two rows of each 32-lane half, and readlane joins
+// the halves.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t y = shfl_xor_u64(x, o);
+  x = dpp_max_u64<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x = dpp_max_u64<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x = dpp_max_u64<0x141>(x);  // row_half_mirror
+  x = dpp_max_u64<0x140>(x);  // row_mirror
+  {
+    const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
+    const uint64_t y = join_u64((uint32_t)__builtin_amdgcn_ds_swizzle(lo, 0x401F),
+                                (uint32_t)__builtin_amdgcn_ds_swizzle(hi, 0x401F));
     x = y > x ? y : x;
   }
-  return x;
+  const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
+  const uint64_t a = join_u64((uint32_t)__builtin_amdgcn_readlane(lo, 0),
+                              (uint32_t)__builtin_amdgcn_readlane(hi, 0));
+  const uint64_t b = join_u64((uint32_t)__builtin_amdgcn_readlane(lo, 32),
+                              (uint32_t)__builtin_amdgcn_readlane(hi, 32));
+  return a > b ? a : b;
 }
 
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -311,7 +311,7 @@ hipError_t launch_index_pool(const void* q_idx, const void* k_idx, int64_t q_sta
 // ~b so that on equal scores the lower block ranks higher).  Every lane
 // scans a strided slice of the row and keeps its best LM keys in a sorted
 // register list; the wave then pops the global best k-1 keys one at a time
-// (a cross-lane max per pop).  The local block is added and the k ids are
+// (a cross-lane max per pop, by DPP and ds_swizzle exchanges).  The local block is added and the k ids are
 // written in ascending order.
 // ---------------------------------------------------------------------------
 template <int LM>
@@ -364,7 +364,7 @@ __device__ __forceinline__ void topk_row(const float* __restrict__ prow, int lb,
   // ascending order: rank of each of the k ids among lanes 0..k-1
   int rank = 0;
   for (int j = 0; j < k; ++j) {
-    const int o = __shfl(mine, j, kWave);
+    const int o = __builtin_amdgcn_readlane(mine, j);
     rank += o < mine;
   }
   if (lane < k) out[rank] = mine;
