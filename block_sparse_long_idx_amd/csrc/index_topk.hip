@@ -170,17 +170,26 @@ __host__ __forceinline__ int index_grid(int ntiles, int H_kv) {
   return (int)ceil_div(ntiles, per) * per * H_kv;
 }
 
-// Sink of the two-kernel variant: stores the pooled scores, 4 blocks at a
-// time, into P[r][q - q_start][kb].
+// Sink of the two-kernel variant: stores the pooled scores into
+// P[r][q - q_start][kb], 16 blocks (64 contiguous bytes) at a time.  The
+// rows of neighbouring lanes lie a whole row pitch apart, so narrower
+// stores would leave every written line partly filled and multiply the
+// HBM write traffic.  The last group stops at the quad holding block
+// kb_end_w - 1, inside the row (the pitch is a multiple of 4).
 struct PoolStore {
   float* prow;
   bool own_ok;
-  float pend[4];
+  float pend[16];
   __device__ __forceinline__ void operator()(int kb, int kb_end_w, float v) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pend[e] = (kb & 3) == e ? v : pend[e];  // no dynamic index
-    if (own_ok && ((kb & 3) == 3 || kb == kb_end_w - 1))
-      *reinterpret_cast<f32x4*>(prow + (kb & ~3)) = f32x4{pend[0], pend[1], pend[2], pend[3]};
+    for (int e = 0; e < 16; ++e) pend[e] = (kb & 15) == e ? v : pend[e];  // no dynamic index
+    if (own_ok && ((kb & 15) == 15 || kb == kb_end_w - 1)) {
+      f32x4* dst = reinterpret_cast<f32x4*>(prow + (kb & ~15));
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (4 * q <= (kb & 15))
+          dst[q] = f32x4{pend[4 * q], pend[4 * q + 1], pend[4 * q + 2], pend[4 * q + 3]};
+    }
   }
 };
 
@@ -195,8 +204,7 @@ __global__ __launch_bounds__(64 * NW) void index_pool_kernel(
   const int lane = threadIdx.x & 63;
   const int64_t q_own = q_start + (int64_t)tile * (64 * NW) + (threadIdx.x >> 6) * 64 +
                         32 * (lane >> 5) + (lane & 31);
-  PoolStore sink{P + ((int64_t)r * Nq + (q_own - q_start)) * ldp, q_own < q_start + Nq,
-                 {0.f, 0.f, 0.f, 0.f}};
+  PoolStore sink{P + ((int64_t)r * Nq + (q_own - q_start)) * ldp, q_own < q_start + Nq, {}};
   index_sweep<D, NW>(q_idx, k_idx, q_start, Nq, H_kv, r, tile, lds, sink);
 }
 
