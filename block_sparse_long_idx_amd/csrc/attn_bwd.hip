@@ -477,8 +477,11 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(const __bf16* __rest
   const __bf16* src = part + ((iq * k) * H_kv + r) * (DH / 4) * G * 4 + ((int64_t)dq * G + hl) * 4;
   const int64_t slot_stride = (int64_t)H_kv * (DH / 4) * G * 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // each partial is read once: non-temporal loads, four slots in flight
+#pragma unroll 4
   for (int s = 0; s < n_sel; ++s) {
-    const bf16x4 x = *reinterpret_cast<const bf16x4*>(src + s * slot_stride);
+    const bf16x4 x =
+        __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(src + s * slot_stride));
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += bf2f(x[e]);
   }

@@ -62,10 +62,13 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const __bf16* __restri
     const __bf16* base = kseq + (int64_t)blk * kBlock * TE;
     float m = -INFINITY;
     for (int u0 = 0; u0 < iters; u0 += 8) {
+      // the cache's index keys are read exactly once: non-temporal loads
+      // (measured 5.7 -> 6.5 TB/s on the 32 x 1M scan)
       bf16x8 x[8];
 #pragma unroll
       for (int v = 0; v < 8; ++v)
-        x[v] = *reinterpret_cast<const bf16x8*>(base + (int64_t)512 * (u0 + v));
+        x[v] = __builtin_nontemporal_load(
+            reinterpret_cast<const bf16x8*>(base + (int64_t)512 * (u0 + v)));
 #pragma unroll
       for (int v = 0; v < 8; ++v) {
         float s = dot8(x[v], q);
