@@ -41,29 +41,34 @@ __device__ __forceinline__ int kswz(int row) {
 }
 
 // The sweep shared by both Index-Branch variants.  For every key block kb
-// it hands the pooled score of the lane's own query to `sink(kb, v)`; the
-// lane owns query q_own = qw0 + 32*h + n (lane half h <-> column group h).
-template <int D, int NW, typename Sink>
+// it hands the pooled scores of the lane's own queries to `sink(kb, v)`.
+// A wave takes CG column groups of 32 queries (32*CG queries); lane half h
+// owns the queries of column groups h, h+2, ..: q_own[j] = qw0 + 32*(2j+h)
+// + n, v[j] its score.
+template <int D, int NW, int CG, typename Sink>
 __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
                                             const __bf16* __restrict__ k_idx, int64_t q_start,
                                             int64_t Nq, int H_kv, int r, int tile,
                                             __bf16 (*lds)[128 * D], Sink& sink) {
+  static_assert(CG == 2 || CG == 4, "column groups per wave");
   constexpr int S = D / 16;   // MFMA k-steps
   constexpr int CH = D / 8;   // 16-byte chunks per key row
+  constexpr int QW = 32 * CG;  // queries per wave
+  constexpr int NQ = CG / 2;   // queries per lane
   const int t = threadIdx.x;
   const int wave = t >> 6, lane = t & 63;
   const int h = lane >> 5, n = lane & 31;
   const int64_t q_end = q_start + Nq;
-  const int64_t q0 = q_start + (int64_t)tile * (64 * NW);
-  const int64_t qw0 = q0 + wave * 64;
-  const int64_t q_last = min(q0 + 64 * NW - 1, q_end - 1);
+  const int64_t q0 = q_start + (int64_t)tile * (QW * NW);
+  const int64_t qw0 = q0 + wave * QW;
+  const int64_t q_last = min(q0 + QW * NW - 1, q_end - 1);
   const int kb_end = (int)(q_last / kBlock);
-  const int kb_end_w = qw0 < q_end ? (int)(min(qw0 + 63, q_end - 1) / kBlock) : 0;
+  const int kb_end_w = qw0 < q_end ? (int)(min(qw0 + QW - 1, q_end - 1) / kBlock) : 0;
 
-  // Query operand (MFMA B: 16 d x 32 queries), two column groups.
-  bf16x8 qb[2][S];
+  // Query operand (MFMA B: 16 d x 32 queries), CG column groups.
+  bf16x8 qb[CG][S];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < CG; ++c) {
     const int64_t q = qw0 + 32 * c + n;
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -97,48 +102,78 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
   __builtin_amdgcn_s_waitcnt(0);  // block 0 and the query operand
   __syncthreads();
 
-  // The sink takes block kb-1's pooled score while block kb's MFMAs are in
+  // The sink takes block kb-1's pooled scores while block kb's MFMAs are in
   // flight, so its VALU work can issue under them.
   int kb_prev = -1;
-  float v_prev = -INFINITY;
+  float v_prev[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) v_prev[j] = -INFINITY;
   for (int kb = 0; kb < kb_end; ++kb) {
     const int buf = kb & 1;
     if (kb + 1 < kb_end) dma(kb + 1, buf ^ 1);
     if (kb < kb_end_w) {
-      float m0 = -INFINITY, m1 = -INFINITY;
-      // key-row groups in pairs: the second group's MFMAs overlap the first
-      // group's max-pool
+      float m[CG];
 #pragma unroll
-      for (int g0 = 0; g0 < 4; g0 += 2) {
-        f32x16 acc[2][2];
+      for (int c = 0; c < CG; ++c) m[c] = -INFINITY;
+      if constexpr (CG == 2) {
+        // key-row groups in pairs: the second group's MFMAs overlap the
+        // first group's max-pool
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int row = 32 * (g0 + g) + n;
+        for (int g0 = 0; g0 < 4; g0 += 2) {
+          f32x16 acc[2][2];
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int row = 32 * (g0 + g) + n;
+            bf16x8 a[S];
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+              a[s] = *reinterpret_cast<const bf16x8*>(
+                  &lds[buf][row * D + 8 * (((D / 16) * h + s) ^ kswz<D>(row))]);
+            acc[g][0] = acc[g][1] = f32x16{};
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+              acc[g][0] = mfma32(a[s], qb[0][s], acc[g][0]);
+              acc[g][1] = mfma32(a[s], qb[1][s], acc[g][1]);
+            }
+          }
+          if (g0 == 0 && kb_prev >= 0) sink(kb_prev, kb_end_w, v_prev);
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              m[0] = fmaxf(m[0], acc[g][0][j]);
+              m[1] = fmaxf(m[1], acc[g][1][j]);
+            }
+        }
+      } else {
+        // one key-row group at a time: each LDS fragment feeds CG MFMAs
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row = 32 * g + n;
           bf16x8 a[S];
 #pragma unroll
           for (int s = 0; s < S; ++s)
             a[s] = *reinterpret_cast<const bf16x8*>(
                 &lds[buf][row * D + 8 * (((D / 16) * h + s) ^ kswz<D>(row))]);
-          acc[g][0] = acc[g][1] = f32x16{};
+          f32x16 acc[CG];
 #pragma unroll
-          for (int s = 0; s < S; ++s) {
-            acc[g][0] = mfma32(a[s], qb[0][s], acc[g][0]);
-            acc[g][1] = mfma32(a[s], qb[1][s], acc[g][1]);
-          }
+          for (int c = 0; c < CG; ++c) acc[c] = f32x16{};
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int c = 0; c < CG; ++c) acc[c] = mfma32(a[s], qb[c][s], acc[c]);
+          if (g == 0 && kb_prev >= 0) sink(kb_prev, kb_end_w, v_prev);
+#pragma unroll
+          for (int c = 0; c < CG; ++c)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) m[c] = fmaxf(m[c], acc[c][j]);
         }
-        if (g0 == 0 && kb_prev >= 0) sink(kb_prev, kb_end_w, v_prev);
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            m0 = fmaxf(m0, acc[g][0][j]);
-            m1 = fmaxf(m1, acc[g][1][j]);
-          }
       }
-      m0 = fmaxf(m0, __shfl_xor(m0, 32, kWave));
-      m1 = fmaxf(m1, __shfl_xor(m1, 32, kWave));
+#pragma unroll
+      for (int c = 0; c < CG; ++c) m[c] = fmaxf(m[c], __shfl_xor(m[c], 32, kWave));
       kb_prev = kb;
-      v_prev = h ? m1 : m0;
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) v_prev[j] = h ? m[2 * j + 1] : m[2 * j];
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of block kb+1 is in LDS
     __syncthreads();
@@ -180,9 +215,9 @@ struct PoolStore {
   float* prow;
   bool own_ok;
   float pend[16];
-  __device__ __forceinline__ void operator()(int kb, int kb_end_w, float v) {
+  __device__ __forceinline__ void operator()(int kb, int kb_end_w, const float (&v)[1]) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) pend[e] = (kb & 15) == e ? v : pend[e];  // no dynamic index
+    for (int e = 0; e < 16; ++e) pend[e] = (kb & 15) == e ? v[0] : pend[e];  // no dynamic index
     if (own_ok && ((kb & 15) == 15 || kb == kb_end_w - 1)) {
       f32x4* dst = reinterpret_cast<f32x4*>(prow + (kb & ~15));
 #pragma unroll
@@ -205,72 +240,83 @@ __global__ __launch_bounds__(64 * NW) void index_pool_kernel(
   const int64_t q_own = q_start + (int64_t)tile * (64 * NW) + (threadIdx.x >> 6) * 64 +
                         32 * (lane >> 5) + (lane & 31);
   PoolStore sink{P + ((int64_t)r * Nq + (q_own - q_start)) * ldp, q_own < q_start + Nq, {}};
-  index_sweep<D, NW>(q_idx, k_idx, q_start, Nq, H_kv, r, tile, lds, sink);
+  index_sweep<D, NW, 2>(q_idx, k_idx, q_start, Nq, H_kv, r, tile, lds, sink);
 }
 
 // Sink of the fused variant: a running Top-LM list of (score, block) per
 // query, sorted by score, descending.  Blocks arrive in ascending order and
 // a new score must beat an equal one strictly, so among equal scores the
 // lower block stays ahead (ties go to the lower block index).
-template <int LM>
+template <int LM, int NQ>
 struct TopkKeep {
-  int lb_own;
-  float sc[LM];
-  int bk[LM];
-  __device__ __forceinline__ void operator()(int kb, int, float v) {
-    // A block that must not enter (the local block or later) becomes -inf.
-    v = kb < lb_own ? v : -INFINITY;
-    if (v > sc[LM - 1]) {
+  int lb_own[NQ];
+  float sc[NQ][LM];
+  int bk[NQ][LM];
+  __device__ __forceinline__ void operator()(int kb, int, const float (&vin)[NQ]) {
 #pragma unroll
-      for (int j = LM - 1; j > 0; --j) {
-        const bool up = v > sc[j - 1];
-        const bool here = v > sc[j];
-        sc[j] = up ? sc[j - 1] : (here ? v : sc[j]);
-        bk[j] = up ? bk[j - 1] : (here ? kb : bk[j]);
+    for (int q = 0; q < NQ; ++q) {
+      // A block that must not enter (the local block or later) becomes -inf.
+      const float v = kb < lb_own[q] ? vin[q] : -INFINITY;
+      if (v > sc[q][LM - 1]) {
+#pragma unroll
+        for (int j = LM - 1; j > 0; --j) {
+          const bool up = v > sc[q][j - 1];
+          const bool here = v > sc[q][j];
+          sc[q][j] = up ? sc[q][j - 1] : (here ? v : sc[q][j]);
+          bk[q][j] = up ? bk[q][j - 1] : (here ? kb : bk[q][j]);
+        }
+        bk[q][0] = v > sc[q][0] ? kb : bk[q][0];
+        sc[q][0] = v > sc[q][0] ? v : sc[q][0];
       }
-      bk[0] = v > sc[0] ? kb : bk[0];
-      sc[0] = v > sc[0] ? v : sc[0];
     }
   }
 };
 
-template <int D, int NW, int LM>
+template <int D, int NW, int CG, int LM>
 __global__ __launch_bounds__(64 * NW) void index_topk_fused_kernel(
     const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx, int64_t q_start,
     int64_t Nq, int H_kv, int ntiles, int k, int32_t* __restrict__ sel) {
+  constexpr int NQ = CG / 2;
   __shared__ __attribute__((aligned(16))) __bf16 lds[2][128 * D];
   int r, tile;
   if (!index_tile_of(blockIdx.x, ntiles, H_kv, r, tile)) return;
   const int lane = threadIdx.x & 63;
-  const int64_t q_own = q_start + (int64_t)tile * (64 * NW) + (threadIdx.x >> 6) * 64 +
-                        32 * (lane >> 5) + (lane & 31);
-  const bool own_ok = q_own < q_start + Nq;
-  TopkKeep<LM> keep;
-  keep.lb_own = own_ok ? (int)(q_own / kBlock) : 0;
+  const int64_t qw0 = q_start + (int64_t)tile * (32 * CG * NW) + (threadIdx.x >> 6) * (32 * CG);
+  TopkKeep<LM, NQ> keep;
 #pragma unroll
-  for (int j = 0; j < LM; ++j) {
-    keep.sc[j] = -INFINITY;
-    keep.bk[j] = -1;
-  }
-  index_sweep<D, NW>(q_idx, k_idx, q_start, Nq, H_kv, r, tile, lds, keep);
-  if (!own_ok) return;
-  int32_t* out = sel + ((q_own - q_start) * H_kv + r) * k;
-  const int K1 = k - 1, lb = keep.lb_own;
-  if (lb <= K1) {
-    for (int t = 0; t < k; ++t) out[t] = t <= lb ? t : -1;
-    return;
-  }
-  // the K1 best blocks in ascending order, then the local block (largest id)
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t q_own = qw0 + 32 * (2 * q + (lane >> 5)) + (lane & 31);
+    keep.lb_own[q] = q_own < q_start + Nq ? (int)(q_own / kBlock) : 0;
 #pragma unroll
-  for (int j = 0; j < LM; ++j) {
-    if (j < K1) {
-      int rank = 0;
-#pragma unroll
-      for (int i = 0; i < LM; ++i) rank += (i < K1) & (keep.bk[i] < keep.bk[j]);
-      out[rank] = keep.bk[j];
+    for (int j = 0; j < LM; ++j) {
+      keep.sc[q][j] = -INFINITY;
+      keep.bk[q][j] = -1;
     }
   }
-  out[K1] = lb;
+  index_sweep<D, NW, CG>(q_idx, k_idx, q_start, Nq, H_kv, r, tile, lds, keep);
+  const int K1 = k - 1;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int64_t q_own = qw0 + 32 * (2 * q + (lane >> 5)) + (lane & 31);
+    if (q_own >= q_start + Nq) continue;
+    int32_t* out = sel + ((q_own - q_start) * H_kv + r) * k;
+    const int lb = keep.lb_own[q];
+    if (lb <= K1) {
+      for (int t = 0; t < k; ++t) out[t] = t <= lb ? t : -1;
+      continue;
+    }
+    // the K1 best blocks in ascending order, then the local block (largest id)
+#pragma unroll
+    for (int j = 0; j < LM; ++j) {
+      if (j < K1) {
+        int rank = 0;
+#pragma unroll
+        for (int i = 0; i < LM; ++i) rank += (i < K1) & (keep.bk[q][i] < keep.bk[q][j]);
+        out[rank] = keep.bk[q][j];
+      }
+    }
+    out[K1] = lb;
+  }
 }
 
 // Waves per index work-group: 8 when 512-query tiles still give at least
@@ -425,26 +471,31 @@ hipError_t launch_topk_decode(const float* P, int64_t ldp, int B, int H_kv, int 
   return launch_topk(P, ldp, (int64_t)B * H_kv, 1, H_kv, 0, nblk, k, sel, stream);
 }
 
-template <int D, int NW>
+template <int D, int NW, int CG>
 static void launch_fused_dn(const __bf16* qi, const __bf16* ki, int64_t q_start, int64_t Nq,
                             int H_kv, int k, int32_t* sel, hipStream_t stream) {
-  const int ntiles = (int)ceil_div(Nq, (int64_t)(64 * NW));
+  const int ntiles = (int)ceil_div(Nq, (int64_t)(32 * CG * NW));
   dim3 grid(index_grid(ntiles, H_kv)), block(64 * NW);
   if (k <= 8)
-    index_topk_fused_kernel<D, NW, 7><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
+    index_topk_fused_kernel<D, NW, CG, 7><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
   else if (k <= 16)
-    index_topk_fused_kernel<D, NW, 15><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
+    index_topk_fused_kernel<D, NW, CG, 15><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
   else
-    index_topk_fused_kernel<D, NW, 31><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
+    index_topk_fused_kernel<D, NW, CG, 31><<<grid, block, 0, stream>>>(qi, ki, q_start, Nq, H_kv, ntiles, k, sel);
 }
 
 template <int D>
 static void launch_fused_d(const __bf16* qi, const __bf16* ki, int64_t q_start, int64_t Nq,
                            int H_kv, int k, int32_t* sel, hipStream_t stream) {
-  if (D < 128 && index_waves(Nq, H_kv, D) == 8)
-    launch_fused_dn<D, D < 128 ? 8 : 4>(qi, ki, q_start, Nq, H_kv, k, sel, stream);
+  // 128 queries per wave (each staged key block then serves 1024 queries)
+  // while 1024-query tiles still give every CU a work-group; the lists of
+  // k > 16 would not fit the registers of two queries per lane
+  if (D <= 64 && k <= 16 && ceil_div(Nq, (int64_t)1024) * H_kv >= device_cus())
+    launch_fused_dn<D, 8, D <= 64 ? 4 : 2>(qi, ki, q_start, Nq, H_kv, k, sel, stream);
+  else if (D < 128 && index_waves(Nq, H_kv, D) == 8)
+    launch_fused_dn<D, D < 128 ? 8 : 4, 2>(qi, ki, q_start, Nq, H_kv, k, sel, stream);
   else
-    launch_fused_dn<D, 4>(qi, ki, q_start, Nq, H_kv, k, sel, stream);
+    launch_fused_dn<D, 4, 2>(qi, ki, q_start, Nq, H_kv, k, sel, stream);
 }
 
 hipError_t launch_index_topk_fused(const void* q_idx, const void* k_idx, int64_t q_start,
