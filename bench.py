@@ -509,9 +509,12 @@ def main():
     log(f"[bench] {ms:.2f} ms/step; stages " +
         ", ".join(f"{n} {s:.2f} ms" for n, s in zip(stage_names, stages)))
 
-    # roofline of the dominant stage (the fused Index Branch is one kernel)
-    dom = max(range(3), key=lambda s: stages[s])
-    if dom == 0 and args.fused:
+    # Roofline of the dominant kernel.  With the fused Index Branch that is
+    # its single launch per step, the largest kernel of the step: the Main
+    # Branch stage is three kernels per query chunk (work list, KV-outer
+    # attention, combine), the largest of which takes ~2/3 of the stage
+    # (kernel trace in profiles/prefill_1m_kernel_stats.md).
+    if args.fused:
         ach = index_f / (stages[0] / 1e3) / 1e12
         roof = {"kernel": "index_topk_fused_kernel", "bound": "mfma",
                 "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -521,8 +524,22 @@ def main():
                               "algorithmic flops (H_kv*d_idx*N^2) / its event time; traffic "
                               "in HBM bytes per launch"}
     else:
-        roof = {"kernel": stage_names[dom], "bound": "hbm", "achieved": None,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": None, "traffic": None}
+        roof = {"kernel": "index_pool_kernel + topk_kernel", "bound": "mfma", "achieved": None,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": None, "traffic": None}
+    # The Main Branch stage against HBM: per non-local (query, head, block) Q
+    # is gathered (2 d_h B), the bf16 partial written and read back (4 d_h B)
+    # with its fp32 lse (8 B); per (query, head) the combine reads the local
+    # block's Q (2 d_h B) and writes O (4 d_h B) and lse (4 B).
+    main_bytes = 0
+    for q0, nq in chunks_of(cfg):
+        nl = (msa.selection_nnz(q0, nq, cfg.H_kv, cfg.k) - nq * cfg.H_kv) * (cfg.H_q // cfg.H_kv)
+        main_bytes += nl * (6 * cfg.d_h + 8) + nq * cfg.H_q * (6 * cfg.d_h + 4)
+    main_gbs = main_bytes / (stages[2] / 1e3) / 1e9
+    roof_main = {"stage": "sparse_attn_fwd", "kernels": "build_items_kernel, "
+                 "attn_kv_outer_kernel, combine_local_kernel per query chunk",
+                 "bound": "hbm", "achieved": round(main_gbs, 1), "peak": PEAK_HBM_GBS,
+                 "unit": "GB/s", "frac": round(main_gbs / PEAK_HBM_GBS, 4),
+                 "algorithmic_bytes_per_step": main_bytes}
 
     out = {
         "metric": "MSA prefill tokens/s + effective TFLOP/s (% bf16 MFMA peak) at 128K and 1M",
@@ -544,6 +561,7 @@ def main():
                                    "index": round(index_f / 1e12, 3)},
         "stage_ms": {n: round(s, 3) for n, s in zip(stage_names, stages)},
         "roofline": roof,
+        "roofline_main_branch": roof_main,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on {args.cpu_rows} sampled rows")
