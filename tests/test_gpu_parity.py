@@ -82,6 +82,34 @@ def test_index_topk_stage(oracle_lib, case):
         msa.set_option(msa.OPT_INDEX_FUSED, old)
 
 
+# Shapes that take the fused kernel's 128-queries-per-wave form (1024-query
+# tiles, two Top-k lists per lane): chosen when ceil(Nq/1024) * H_kv covers
+# every compute unit (256 on MI355X), d_idx <= 64 and k <= 16.  Both end in
+# a ragged tile; the second starts off a block edge.
+WIDE_CASES = [
+    # N, H_kv, d_idx, k, n_hot, q_start, Nq
+    (4200, 64, 64, 16, 3, 0, 4200),
+    (4600, 64, 32, 8, 2, 700, 3900),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: "N%d_Hkv%d_di%d_k%d_qs%d" % (c[0], c[1], c[2], c[3], c[5]))
+def test_index_topk_wide_tiles(oracle_lib, case):
+    N, H_kv, d_idx, k, n_hot, q_start, Nq = case
+    say("index_topk wide tiles", case)
+    t = make_prefill_inputs(N, H_kv, H_kv, 64, d_idx, n_hot=n_hot, seed=N + 5 * k)
+    rows = np.arange(q_start, q_start + Nq)
+    ref = oracle_lib.select(bf16_bits(t["q_idx"])[rows], bf16_bits(t["k_idx"]), rows, k)
+    old = msa.get_option(msa.OPT_INDEX_FUSED)
+    try:
+        msa.set_option(msa.OPT_INDEX_FUSED, 1)
+        sel = msa.index_topk(t["q_idx"].cuda(), t["k_idx"].cuda(), k, q_start=q_start, Nq=Nq)
+        torch.cuda.synchronize()
+    finally:
+        msa.set_option(msa.OPT_INDEX_FUSED, old)
+    np.testing.assert_array_equal(sel.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("case", STAGE_CASES, ids=lambda c: "N%d_k%d_qs%d" % (c[0], c[5], c[7]))
 def test_invert_stage(oracle_lib, case):
     N, H_q, H_kv, d_h, d_idx, k, n_hot, q_start, Nq = case
