@@ -512,8 +512,7 @@ def main():
     # Roofline of the dominant kernel.  With the fused Index Branch that is
     # its single launch per step, the largest kernel of the step: the Main
     # Branch stage is three kernels per query chunk (work list, KV-outer
-    # attention, combine), the largest of which takes ~2/3 of the stage
-    # (kernel trace in profiles/prefill_1m_kernel_stats.md).
+    # attention, combine), the largest of which takes ~2/3 of the stage.
     if args.fused:
         ach = index_f / (stages[0] / 1e3) / 1e12
         roof = {"kernel": "index_topk_fused_kernel", "bound": "mfma",
