@@ -14,8 +14,8 @@ import pytest
 import torch
 
 from block_sparse_long_idx_amd import msa
-from block_sparse_long_idx_amd.synth import (CONFIGS, bf16_bits, inputs_for,
-                                             make_decode_inputs,
+from block_sparse_long_idx_amd.synth import (CONFIGS, MsaConfig, bf16_bits,
+                                             inputs_for, make_decode_inputs,
                                              make_prefill_inputs, sample_rows)
 
 pytestmark = pytest.mark.gpu
@@ -282,6 +282,40 @@ def test_full_1m(oracle_lib, index_variant):
     Index Branch launch over all 1,048,576 queries, then the inverted index
     and the Main Branch per 65,536-query chunk."""
     _full_prefill_check(oracle_lib, CONFIGS["1m"], 256)
+
+
+# The largest key range the library accepts: 16,384 blocks of 128 tokens.
+# k = 32 runs the 64-queries-per-wave index kernel, k = 16 the
+# 128-queries-per-wave one.
+MAX_BLOCK_CASES = [
+    MsaConfig("max_blocks_k32", N=16384 * 128, H_q=4, H_kv=1, d_h=64, d_idx=32,
+              k=32, n_hot=16, chunk=131072, seed=1006),
+    MsaConfig("max_blocks_k16", N=16384 * 128 - 77, H_q=8, H_kv=2, d_h=128,
+              d_idx=64, k=16, n_hot=8, chunk=131072, seed=1007),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", MAX_BLOCK_CASES, ids=lambda c: c.name)
+def test_max_block_count(oracle_lib, index_variant, cfg):
+    assert cfg.nblk == 16384
+    _full_prefill_check(oracle_lib, cfg, 96)
+
+
+@pytest.mark.slow
+def test_decode_max_block_count(oracle_lib):
+    B, N, H_q, H_kv, d_h, d_idx, k = 2, 16384 * 128, 8, 2, 128, 64, 32
+    say("decode max blocks", B, N)
+    t = make_decode_inputs(B, N, H_q, H_kv, d_h, d_idx, seed=1008, device="cuda")
+    scale = 1.0 / math.sqrt(d_h)
+    sel, O, lse = msa.decode(t["q"], t["q_idx"], t["K"], t["V"], t["k_idx"], k, scale=scale)
+    torch.cuda.synchronize()
+    for b in range(B):
+        u = {n: bf16_bits(t[n][b]) for n in t}
+        s_ref, O_ref, l_ref = oracle_lib.decode_one(u["q"], u["q_idx"], u["K"], u["V"],
+                                                    u["k_idx"], k, scale)
+        np.testing.assert_array_equal(sel[b].cpu().numpy(), s_ref)
+        assert_attn_close(O[b].cpu().numpy(), O_ref, lse[b].cpu().numpy(), l_ref)
 
 
 @pytest.mark.slow
