@@ -37,7 +37,9 @@
  * Supported shapes: B_k = 128; d_h in {64, 128}; d_idx in {32, 64, 128};
  * 1 <= k <= 32; H_q a multiple of H_kv with G = H_q / H_kv <= 64;
  * H_kv <= 64; every block count ceil(N / B_k) <= 16384; every selection
- * nnz < 2^31.
+ * nnz < 2^31.  Row counts (Nq, N, B) are at least 1 and q_start >= 0: an
+ * empty chunk is MSA_ERR_INVALID_ARG (msa_prefill_varlen alone accepts
+ * empty sequences within its batch).
  *
  * Determinism: every output is bitwise identical from run to run.
  */

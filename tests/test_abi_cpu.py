@@ -167,3 +167,27 @@ def test_varlen_and_cached_reject(lib):
     st = lib.msa_prefill_cached(FAKE, FAKE, FAKE, FAKE, FAKE, 1000, 0, 0, 16, 4, 128, 64, 128, 8,
                                 0.1, NULL, FAKE, NULL, FAKE, 1 << 30, NULL)
     assert st == msa.ERR_INVALID_ARG
+
+
+def test_empty_chunks_rejected(lib):
+    """Every chunk-level entry point refuses Nq = 0 (and the front-end N = 0)
+    on the host, before any device work."""
+    E = msa.ERR_INVALID_ARG
+    assert lib.msa_invert_index(FAKE, 0, 0, 4, 128, 16, FAKE, FAKE, FAKE, FAKE,
+                                1 << 30, NULL) == E
+    assert ">= 1" in _err(lib), _err(lib)
+    assert lib.msa_sparse_attn_fwd(*[FAKE] * 6, 0, 0, 128, 8, 4, 128, 128, 4, 0.1, FAKE,
+                                   NULL, FAKE, 1 << 30, NULL) == E
+    assert ">= 1" in _err(lib), _err(lib)
+    assert lib.msa_sparse_attn_bwd(*[FAKE] * 9, 0, 0, 128, 8, 4, 128, 128, 4, 0.1, FAKE,
+                                   FAKE, FAKE, FAKE, 1 << 30, NULL) == E
+    assert ">= 1" in _err(lib), _err(lib)
+    assert lib.msa_index_kl(*[FAKE] * 8, 0, 0, 128, 8, 4, 128, 64, 128, 4, 0.1, FAKE,
+                            NULL, FAKE, 1 << 30, NULL) == E
+    assert ">= 1" in _err(lib), _err(lib)
+    assert lib.msa_prefill_cached(*[FAKE] * 5, 128, 0, 0, 8, 4, 128, 64, 128, 4, 0.1, NULL,
+                                  FAKE, NULL, FAKE, 1 << 30, NULL) == E
+    assert ">= 1" in _err(lib), _err(lib)
+    assert lib.msa_index_frontend(*[FAKE] * 5, 0, 0, 256, 4, 64, 64, 1e4, 1e-6, FAKE, FAKE,
+                                  NULL) == E
+    assert ">= 1" in _err(lib), _err(lib)
