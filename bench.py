@@ -424,7 +424,7 @@ def time_decode(cfg, steps, warmup):
     t = inputs_for(cfg, device="cuda")
     dev = t["q"].device
     B, N = cfg.batch, cfg.N
-    ws = torch.empty(msa.decode_workspace_bytes(B, N, cfg.H_q, cfg.H_kv, cfg.d_h, cfg.k),
+    ws = torch.empty(msa.decode_workspace_bytes(B, N, cfg.H_q, cfg.H_kv, cfg.d_h, cfg.d_idx, cfg.k),
                      dtype=torch.uint8, device=dev)
     sel = torch.empty((B, cfg.H_kv, cfg.k), dtype=torch.int32, device=dev)
     O = torch.empty((B, cfg.H_q, cfg.d_h), dtype=torch.float32, device=dev)

@@ -205,8 +205,9 @@ __device__ __forceinline__ TileRow tile_row(const AttnSmem<DH>& sm, int nrows, i
 }
 
 // Q operand of the lane's row (MFMA B: 16 d x 32 rows per k-step).  Rows
-// past the item's end read row 0 of Q instead (always valid memory): a row
-// only feeds its own MFMA column, and such rows are never stored.
+// past the item's end carry the item's first query row (tile_row), which
+// lies inside the chunk and so is valid memory: a row only feeds its own
+// MFMA column, and such rows are never stored.
 template <int DH>
 __device__ __forceinline__ void load_q(bf16x8 (&qb)[DH / 16], const __bf16* __restrict__ Q,
                                        const TileRow& t, int H_q, int h) {

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <string>
 
@@ -14,11 +15,26 @@
 namespace {
 
 thread_local std::string g_err;
-int64_t g_opt_fused = 1;
-int64_t g_opt_chunk = 1024;
+// Tuning knobs.  Each entry point reads them once, when it starts, and
+// uses that snapshot throughout; no workspace size depends on them.
+std::atomic<int64_t> g_opt_fused{1};
+std::atomic<int64_t> g_opt_chunk{1024};
 
 constexpr int kB = 128;
 constexpr size_t kAlign = 256;
+// Smallest accepted KV-outer work item: work lists are sized for it, so a
+// workspace fits every item size the option can take.
+constexpr int kMinItem = 128;
+
+struct Opts {
+  bool fused;  // Index Branch as one fused kernel
+  int item;    // query positions per KV-outer work item
+};
+
+Opts opts_now() {
+  return Opts{g_opt_fused.load(std::memory_order_relaxed) != 0,
+              (int)g_opt_chunk.load(std::memory_order_relaxed)};
+}
 
 msa_status fail(msa_status st, const char* fmt, ...) {
   char buf[512];
@@ -91,9 +107,9 @@ size_t index_ws(int64_t q_start, int64_t Nq, int H_kv) {
 }
 
 msa_status run_index_topk(const void* q_idx, const void* k_idx, int64_t q_start, int64_t Nq,
-                          int H_kv, int d_idx, int k, int32_t* sel, void* ws,
+                          int H_kv, int d_idx, int k, int32_t* sel, void* ws, bool fused,
                           hipStream_t s) {
-  if (g_opt_fused)
+  if (fused)
     return hip_status(
         msa::launch_index_topk_fused(q_idx, k_idx, q_start, Nq, H_kv, d_idx, k, sel, s),
         "index/top-k (fused) launch");
@@ -129,7 +145,7 @@ AttnWs attn_layout(void* ws, int64_t q_start, int64_t Nq, int H_q, int H_kv, int
   const int64_t nnz = nnz_of(q_start, Nq, H_kv, kB, k);
   AttnWs w;
   Carve c(ws);
-  w.max_items = msa::attn_max_items((int64_t)H_kv * nblk, nnz, (int)g_opt_chunk);
+  w.max_items = msa::attn_max_items((int64_t)H_kv * nblk, nnz, kMinItem);
   w.items = c.take<int4>(sizeof(int4) * (size_t)w.max_items);
   w.n_items = c.take<int32_t>(2 * sizeof(int32_t));  // count, fetch counter
   // Nq * (k-1) slots plus one spare that rows past a work item's end write.
@@ -150,11 +166,11 @@ msa_status check_attn_shapes(int H_q, int H_kv, int d_h) {
 msa_status run_attn(const void* Q, const void* K, const void* V, const int32_t* row_ptr,
                     const int32_t* col, const uint8_t* slot, int64_t q_start, int64_t Nq,
                     int64_t Nk, int H_q, int H_kv, int d_h, int k, float scale, float* O,
-                    float* lse, void* ws, hipStream_t s) {
+                    float* lse, void* ws, int item, hipStream_t s) {
   const int nblk = (int)cdiv(q_start + Nq, kB);
   AttnWs w = attn_layout(ws, q_start, Nq, H_q, H_kv, d_h, k);
   msa_status st = hip_status(msa::launch_build_items(row_ptr, (int64_t)H_kv * nblk, nblk,
-                                                     q_start, Nq, (int)g_opt_chunk, false, w.items,
+                                                     q_start, Nq, item, false, w.items,
                                                      w.n_items, s),
                              "work-list launch");
   if (st) return st;
@@ -215,22 +231,24 @@ PrefillWs prefill_layout(void* ws, int64_t q_begin, int64_t q_end, int64_t chunk
 msa_status prefill_span(const void* Q, const void* K, const void* V, const void* q_idx,
                         const void* k_idx, int64_t q_begin, int64_t q_end, int64_t Nk,
                         int64_t chunk, int H_q, int H_kv, int d_h, int d_idx, int k, float scale,
-                        int32_t* sel, float* O, float* lse, const PrefillWs& w, hipStream_t s) {
+                        int32_t* sel, float* O, float* lse, const PrefillWs& w, const Opts& o,
+                        hipStream_t s) {
   // The fused Index Branch keeps no per-chunk state, so when the caller's
   // sel holds the whole span it runs once over all of it: its work-groups,
   // heaviest first, then balance across what would be separate chunk
   // launches (the early chunks alone leave most of the GPU idle).
-  const bool whole_index = g_opt_fused && sel != nullptr;
+  const bool whole_index = o.fused && sel != nullptr;
   if (whole_index) {
-    msa_status st =
-        run_index_topk(q_idx, k_idx, q_begin, q_end - q_begin, H_kv, d_idx, k, sel, nullptr, s);
+    msa_status st = run_index_topk(q_idx, k_idx, q_begin, q_end - q_begin, H_kv, d_idx, k, sel,
+                                   nullptr, true, s);
     if (st) return st;
   }
   for (int64_t q0 = q_begin; q0 < q_end; q0 += chunk) {
     const int64_t nq = std::min(chunk, q_end - q0), off = q0 - q_begin;
     int32_t* sel_c = sel ? sel + off * H_kv * k : w.sel;
     if (!whole_index) {
-      msa_status st = run_index_topk(q_idx, k_idx, q0, nq, H_kv, d_idx, k, sel_c, w.shared, s);
+      msa_status st =
+          run_index_topk(q_idx, k_idx, q0, nq, H_kv, d_idx, k, sel_c, w.shared, o.fused, s);
       if (st) return st;
     }
     msa_status st;
@@ -240,7 +258,7 @@ msa_status prefill_span(const void* Q, const void* K, const void* V, const void*
                     "inverted-index launch");
     if (st) return st;
     st = run_attn(Q, K, V, w.row_ptr, w.col, w.slot, q0, nq, Nk, H_q, H_kv, d_h, k, scale,
-                  O + off * H_q * d_h, lse ? lse + off * H_q : nullptr, w.shared, s);
+                  O + off * H_q * d_h, lse ? lse + off * H_q : nullptr, w.shared, o.item, s);
     if (st) return st;
   }
   return MSA_OK;
@@ -296,9 +314,10 @@ msa_status msa_index_topk(const void* q_idx, const void* k_idx, int64_t q_start,
   if (msa_status st = check_index_dims(d_idx)) return st;
   if (!q_idx || !k_idx || !sel) return fail(MSA_ERR_INVALID_ARG, "null q_idx, k_idx or sel");
   if (Nk < q_start + Nq) return fail(MSA_ERR_INVALID_ARG, "Nk must be >= q_start + Nq");
-  if (!g_opt_fused && (!ws || ws_bytes < index_ws(q_start, Nq, H_kv)))
+  const Opts o = opts_now();
+  if (!o.fused && (!ws || ws_bytes < index_ws(q_start, Nq, H_kv)))
     return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", index_ws(q_start, Nq, H_kv));
-  msa_status st = run_index_topk(q_idx, k_idx, q_start, Nq, H_kv, d_idx, k, sel, ws,
+  msa_status st = run_index_topk(q_idx, k_idx, q_start, Nq, H_kv, d_idx, k, sel, ws, o.fused,
                                  static_cast<hipStream_t>(stream));
   return st ? st : ok();
 }
@@ -343,7 +362,7 @@ msa_status msa_sparse_attn_fwd(const void* Q, const void* K, const void* V,
   const size_t need = attn_layout(nullptr, q_start, Nq, H_q, H_kv, d_h, k).bytes;
   if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   msa_status st = run_attn(Q, K, V, row_ptr, col, slot, q_start, Nq, Nk, H_q, H_kv, d_h, k,
-                           scale, O, lse, ws, static_cast<hipStream_t>(stream));
+                           scale, O, lse, ws, opts_now().item, static_cast<hipStream_t>(stream));
   return st ? st : ok();
 }
 
@@ -423,7 +442,7 @@ KlWs kl_layout(void* ws, int64_t q_start, int64_t Nq, int H_kv, int k) {
   const int64_t nnz = nnz_of(q_start, Nq, H_kv, kB, k);
   KlWs w;
   Carve c(ws);
-  w.max_items = msa::attn_max_items((int64_t)H_kv * nblk, nnz, (int)g_opt_chunk);
+  w.max_items = msa::attn_max_items((int64_t)H_kv * nblk, nnz, kMinItem);
   w.items = c.take<int4>(sizeof(int4) * (size_t)w.max_items);
   w.n_items = c.take<int32_t>(2 * sizeof(int32_t));
   w.part = c.take<float>(sizeof(float) * 3 * (size_t)Nq * H_kv * k);
@@ -455,7 +474,7 @@ msa_status msa_index_kl(const void* Q, const void* K, const void* q_idx, const v
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nblk = (int)cdiv(q_start + Nq, kB);
   msa_status st = hip_status(msa::launch_build_items(row_ptr, (int64_t)H_kv * nblk, nblk, q_start,
-                                                     Nq, (int)g_opt_chunk, true, w.items,
+                                                     Nq, opts_now().item, true, w.items,
                                                      w.n_items, s),
                              "work-list launch");
   if (st) return st;
@@ -519,7 +538,7 @@ msa_status msa_prefill(const void* Q, const void* K, const void* V, const void* 
   if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   PrefillWs w = prefill_layout(ws, 0, N, chunk, H_q, H_kv, d_h, k, own_sel);
   msa_status st = prefill_span(Q, K, V, q_idx, k_idx, 0, N, N, chunk, H_q, H_kv, d_h, d_idx, k,
-                               scale, sel, O, lse, w, static_cast<hipStream_t>(stream));
+                               scale, sel, O, lse, w, opts_now(), static_cast<hipStream_t>(stream));
   return st ? st : ok();
 }
 
@@ -553,7 +572,7 @@ msa_status msa_prefill_cached(const void* Q, const void* K, const void* V, const
   msa_status st = prefill_span(row_base(Q, q_start, (int64_t)H_q * d_h, 2), K, V,
                                row_base(q_idx, q_start, (int64_t)H_kv * d_idx, 2), k_idx,
                                q_start, q_end, q_end, chunk, H_q, H_kv, d_h, d_idx, k, scale,
-                               sel, O, lse, w, static_cast<hipStream_t>(stream));
+                               sel, O, lse, w, opts_now(), static_cast<hipStream_t>(stream));
   return st ? st : ok();
 }
 
@@ -611,6 +630,7 @@ msa_status msa_prefill_varlen(const void* Q, const void* K, const void* V, const
   if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool own_sel = sel == nullptr;
+  const Opts o = opts_now();
   auto at = [](const void* p, int64_t row, int64_t row_elems) {
     return static_cast<const char*>(p) + row * row_elems * 2;
   };
@@ -624,14 +644,26 @@ msa_status msa_prefill_varlen(const void* Q, const void* K, const void* V, const
         at(V, t0, (int64_t)H_kv * d_h), at(q_idx, t0, (int64_t)H_kv * d_idx),
         at(k_idx, t0, (int64_t)H_kv * d_idx), 0, L, L, c, H_q, H_kv, d_h, d_idx, k, scale,
         own_sel ? nullptr : sel + t0 * H_kv * k, O + t0 * H_q * d_h,
-        lse ? lse + t0 * H_q : nullptr, w, s);
+        lse ? lse + t0 * H_q : nullptr, w, o, s);
     if (st) return st;
   }
   return ok();
 }
 
-size_t msa_decode_workspace_bytes(int B, int64_t N, int H_q, int H_kv, int d_h, int B_k, int k) {
-  if (B < 1 || N < 1 || check_common(0, N, H_kv, B_k, k) || check_attn_shapes(H_q, H_kv, d_h))
+// The split index scan reads whole tokens per KiB load: H_kv * d_idx must
+// divide 512.
+msa_status check_decode_index(int H_kv, int d_idx) {
+  if (msa_status st = check_index_dims(d_idx)) return st;
+  if (512 % (H_kv * d_idx))
+    return fail(MSA_ERR_UNSUPPORTED, "decode needs H_kv * d_idx to divide 512 (got %d * %d)",
+                H_kv, d_idx);
+  return MSA_OK;
+}
+
+size_t msa_decode_workspace_bytes(int B, int64_t N, int H_q, int H_kv, int d_h, int d_idx,
+                                  int B_k, int k) {
+  if (B < 1 || N < 1 || check_common(0, N, H_kv, B_k, k) || check_attn_shapes(H_q, H_kv, d_h) ||
+      check_decode_index(H_kv, d_idx))
     return 0;
   return decode_layout(nullptr, B, N, H_q, H_kv, d_h, k).bytes;
 }
@@ -643,9 +675,7 @@ msa_status msa_decode(const void* q, const void* q_idx, const void* K, const voi
   if (B < 1 || N < 1) return fail(MSA_ERR_INVALID_ARG, "need B >= 1 and N >= 1");
   if (msa_status st = check_common(0, N, H_kv, B_k, k)) return st;
   if (msa_status st = check_attn_shapes(H_q, H_kv, d_h)) return st;
-  if (msa_status st = check_index_dims(d_idx)) return st;
-  if (512 % (H_kv * d_idx))
-    return fail(MSA_ERR_UNSUPPORTED, "decode needs H_kv * d_idx to divide 512");
+  if (msa_status st = check_decode_index(H_kv, d_idx)) return st;
   if (!q || !q_idx || !K || !V || !k_idx || !sel || !O)
     return fail(MSA_ERR_INVALID_ARG, "null q, q_idx, K, V, k_idx, sel or O");
   if (!(scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "scale must be > 0");
@@ -676,12 +706,13 @@ msa_status msa_set_option(int option, int64_t value) {
   switch (option) {
     case MSA_OPT_INDEX_FUSED:
       if (value != 0 && value != 1) return fail(MSA_ERR_INVALID_ARG, "fused must be 0 or 1");
-      g_opt_fused = value;
+      g_opt_fused.store(value, std::memory_order_relaxed);
       return ok();
     case MSA_OPT_ATTN_CHUNK:
-      if (value < 1 || value > msa::attn_max_chunk())
-        return fail(MSA_ERR_INVALID_ARG, "chunk must be in [1, %d]", msa::attn_max_chunk());
-      g_opt_chunk = value;
+      if (value < kMinItem || value > msa::attn_max_chunk())
+        return fail(MSA_ERR_INVALID_ARG, "chunk must be in [%d, %d]", kMinItem,
+                    msa::attn_max_chunk());
+      g_opt_chunk.store(value, std::memory_order_relaxed);
       return ok();
     default:
       return fail(MSA_ERR_INVALID_ARG, "unknown option %d", option);
@@ -691,9 +722,9 @@ msa_status msa_set_option(int option, int64_t value) {
 int64_t msa_get_option(int option) {
   switch (option) {
     case MSA_OPT_INDEX_FUSED:
-      return g_opt_fused;
+      return g_opt_fused.load(std::memory_order_relaxed);
     case MSA_OPT_ATTN_CHUNK:
-      return g_opt_chunk;
+      return g_opt_chunk.load(std::memory_order_relaxed);
     default:
       return -1;
   }

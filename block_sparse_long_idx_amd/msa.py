@@ -54,7 +54,7 @@ def load():
         "msa_prefill_workspace_bytes": ([i64, i64, i32, i32, i32, i32, i32, i32], sz),
         "msa_prefill": ([P, P, P, P, P, i64, i64, i32, i32, i32, i32, i32, i32, f32, P,
                          P, P, P, sz, P], i32),
-        "msa_decode_workspace_bytes": ([i32, i64, i32, i32, i32, i32, i32], sz),
+        "msa_decode_workspace_bytes": ([i32, i64, i32, i32, i32, i32, i32, i32], sz),
         "msa_decode": ([P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32, f32, P, P,
                         P, P, sz, P], i32),
         "msa_index_kl_workspace_bytes": ([i64, i64, i32, i32, i32], sz),
@@ -113,6 +113,30 @@ def _need_cuda(*ts):
                 raise ValueError("tensors must be contiguous")
 
 
+def _expect(name, t, dtype, shape, min_rows=None):
+    """Raise ValueError unless tensor `t` has this dtype and rank, the sizes
+    in `shape` (None = any) and at least `min_rows` leading rows.  The
+    library reads rows by position, so a short tensor would be read past
+    its end on the device."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != len(shape) or any(e is not None and a != e for a, e in zip(t.shape, shape)):
+        want = "[" + ", ".join("*" if e is None else str(e) for e in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+    if min_rows is not None and t.shape[0] < min_rows:
+        raise ValueError(f"{name} has {t.shape[0]} rows, needs at least {min_rows}")
+
+
+def _expect_csr(row_ptr, col, slot, q_start, Nq, H_kv, k, B_k):
+    nblk = (q_start + Nq + B_k - 1) // B_k
+    nnz = load().msa_selection_nnz(q_start, Nq, H_kv, B_k, k)
+    _expect("row_ptr", row_ptr, torch.int32, (None,), H_kv * nblk + 1)
+    _expect("col", col, torch.int32, (None,), nnz)
+    _expect("slot", slot, torch.uint8, (None,), nnz)
+
+
 def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
@@ -132,9 +156,12 @@ def selection_nnz(q_start, Nq, H_kv, k, B_k=B_K) -> int:
 def index_topk(q_idx, k_idx, k, q_start=0, Nq=None, B_k=B_K, sel=None, ws=None):
     """Index Branch for query rows [q_start, q_start+Nq): returns sel int32
     [Nq, H_kv, k].  q_idx/k_idx: bf16 [N, H_kv, d_idx] on the GPU."""
-    _need_cuda(q_idx, k_idx)
+    _need_cuda(q_idx, k_idx, sel)
     N, H_kv, d_idx = k_idx.shape
     Nq = q_idx.shape[0] - q_start if Nq is None else Nq
+    _expect("k_idx", k_idx, torch.bfloat16, (None, H_kv, d_idx), q_start + Nq)
+    _expect("q_idx", q_idx, torch.bfloat16, (None, H_kv, d_idx), q_start + Nq)
+    _expect("sel", sel, torch.int32, (Nq, H_kv, k))
     lib = load()
     if sel is None:
         sel = torch.empty((Nq, H_kv, k), dtype=torch.int32, device=k_idx.device)
@@ -149,8 +176,12 @@ def index_topk(q_idx, k_idx, k, q_start=0, Nq=None, B_k=B_K, sel=None, ws=None):
 def invert_index(sel, q_start=0, B_k=B_K, ws=None, row_ptr=None, col=None, slot=None):
     """Inverted index of sel [Nq, H_kv, k]: (row_ptr, col int32, slot uint8).
     Preallocated outputs may be passed (col/slot with >= nnz entries)."""
-    _need_cuda(sel)
+    _need_cuda(sel, row_ptr, col, slot)
+    _expect("sel", sel, torch.int32, (None, None, None))
     Nq, H_kv, k = sel.shape
+    _expect("row_ptr", row_ptr, torch.int32, (None,))
+    _expect("col", col, torch.int32, (None,))
+    _expect("slot", slot, torch.uint8, (None,))
     lib = load()
     nblk = (q_start + Nq + B_k - 1) // B_k
     nnz = lib.msa_selection_nnz(q_start, Nq, H_kv, B_k, k)
@@ -174,10 +205,16 @@ def invert_index(sel, q_start=0, B_k=B_K, ws=None, row_ptr=None, col=None, slot=
 def sparse_attn_fwd(Q, K, V, row_ptr, col, slot, k, q_start=0, Nq=None, scale=None,
                     B_k=B_K, want_lse=True, O=None, lse=None, ws=None):
     """Main Branch for query rows [q_start, q_start+Nq): (O fp32, lse fp32)."""
-    _need_cuda(Q, K, V, row_ptr, col, slot)
+    _need_cuda(Q, K, V, row_ptr, col, slot, O, lse)
     Nk, H_kv, d_h = K.shape
     H_q = Q.shape[1]
     Nq = Q.shape[0] - q_start if Nq is None else Nq
+    _expect("K", K, torch.bfloat16, (None, H_kv, d_h), q_start + Nq)
+    _expect("V", V, torch.bfloat16, (Nk, H_kv, d_h))
+    _expect("Q", Q, torch.bfloat16, (None, H_q, d_h), q_start + Nq)
+    _expect_csr(row_ptr, col, slot, q_start, Nq, H_kv, k, B_k)
+    _expect("O", O, torch.float32, (Nq, H_q, d_h))
+    _expect("lse", lse, torch.float32, (Nq, H_q))
     scale = 1.0 / math.sqrt(d_h) if scale is None else scale
     lib = load()
     dev = Q.device
@@ -199,10 +236,20 @@ def sparse_attn_bwd(Q, K, V, O, lse, dO, row_ptr, col, slot, k, q_start=0, Nq=No
                     scale=None, B_k=B_K, dQ=None, dK=None, dV=None, ws=None):
     """Main Branch backward for rows [q_start, q_start+Nq): returns (dQ, dK, dV).
     dK and dV are added to (fresh zero tensors when not given)."""
-    _need_cuda(Q, K, V, O, lse, dO, row_ptr, col, slot)
+    _need_cuda(Q, K, V, O, lse, dO, row_ptr, col, slot, dQ, dK, dV)
     Nk, H_kv, d_h = K.shape
     H_q = Q.shape[1]
     Nq = Q.shape[0] - q_start if Nq is None else Nq
+    _expect("K", K, torch.bfloat16, (None, H_kv, d_h), q_start + Nq)
+    _expect("V", V, torch.bfloat16, (Nk, H_kv, d_h))
+    _expect("Q", Q, torch.bfloat16, (None, H_q, d_h), q_start + Nq)
+    _expect("O", O, torch.float32, (Nq, H_q, d_h))
+    _expect("lse", lse, torch.float32, (Nq, H_q))
+    _expect("dO", dO, torch.bfloat16, (Nq, H_q, d_h))
+    _expect_csr(row_ptr, col, slot, q_start, Nq, H_kv, k, B_k)
+    _expect("dQ", dQ, torch.float32, (Nq, H_q, d_h))
+    _expect("dK", dK, torch.float32, (Nk, H_kv, d_h))
+    _expect("dV", dV, torch.float32, (Nk, H_kv, d_h))
     scale = 1.0 / math.sqrt(d_h) if scale is None else scale
     lib = load()
     dev = Q.device
@@ -227,11 +274,19 @@ def prefill_cached(Q, K, V, q_idx, k_idx, k, q_start, chunk=0, scale=None, B_k=B
     """Chunked prefill against a KV cache: Q/q_idx hold the Nq new tokens
     (positions q_start..), K/V/k_idx the cache with them appended.
     Returns (sel, O, lse) for the new tokens."""
-    _need_cuda(Q, K, V, q_idx, k_idx)
+    _need_cuda(Q, K, V, q_idx, k_idx, sel, O, lse)
     Nq, H_q, d_h = Q.shape
     H_kv, d_idx = k_idx.shape[1], k_idx.shape[2]
     if K.shape[0] < q_start + Nq or k_idx.shape[0] < q_start + Nq:
         raise ValueError("the cache must hold q_start + Nq keys")
+    _expect("Q", Q, torch.bfloat16, (Nq, H_q, d_h))
+    _expect("K", K, torch.bfloat16, (None, H_kv, d_h))
+    _expect("V", V, torch.bfloat16, tuple(K.shape))
+    _expect("q_idx", q_idx, torch.bfloat16, (Nq, H_kv, d_idx))
+    _expect("k_idx", k_idx, torch.bfloat16, (None, H_kv, d_idx))
+    _expect("sel", sel, torch.int32, (Nq, H_kv, k))
+    _expect("O", O, torch.float32, (Nq, H_q, d_h))
+    _expect("lse", lse, torch.float32, (Nq, H_q))
     scale = 1.0 / math.sqrt(d_h) if scale is None else scale
     lib = load()
     dev = Q.device
@@ -254,9 +309,17 @@ def prefill_varlen(Q, K, V, q_idx, k_idx, cu_seqlens, k, chunk=0, scale=None, B_
                    sel=None, O=None, lse=None, want_lse=True, ws=None):
     """Varlen batched prefill of packed sequences; cu_seqlens is a host
     sequence of B+1 prefix sums.  Returns (sel, O, lse) for all tokens."""
-    _need_cuda(Q, K, V, q_idx, k_idx)
+    _need_cuda(Q, K, V, q_idx, k_idx, sel, O, lse)
     T, H_q, d_h = Q.shape
     H_kv, d_idx = k_idx.shape[1], k_idx.shape[2]
+    _expect("Q", Q, torch.bfloat16, (T, H_q, d_h))
+    _expect("K", K, torch.bfloat16, (T, H_kv, d_h))
+    _expect("V", V, torch.bfloat16, (T, H_kv, d_h))
+    _expect("q_idx", q_idx, torch.bfloat16, (T, H_kv, d_idx))
+    _expect("k_idx", k_idx, torch.bfloat16, (T, H_kv, d_idx))
+    _expect("sel", sel, torch.int32, (T, H_kv, k))
+    _expect("O", O, torch.float32, (T, H_q, d_h))
+    _expect("lse", lse, torch.float32, (T, H_q))
     cu = (ctypes.c_int64 * len(cu_seqlens))(*[int(x) for x in cu_seqlens])
     B = len(cu_seqlens) - 1
     if int(cu_seqlens[-1]) != T:
@@ -284,8 +347,15 @@ def index_frontend(hidden, Wq, Wk, gq, gk, H_kv, d_idx, pos0=0, rope_dim=64,
     """Index Branch front-end: hidden [N, d_model] bf16 -> (q_idx, k_idx)
     [N, H_kv, d_idx] bf16 by linear projection, per-group RMS norm and RoPE
     over the first rope_dim entries at positions pos0 + i."""
-    _need_cuda(hidden, Wq, Wk, gq, gk)
+    _need_cuda(hidden, Wq, Wk, gq, gk, q_idx, k_idx)
+    _expect("hidden", hidden, torch.bfloat16, (None, None))
     N, d_model = hidden.shape
+    _expect("Wq", Wq, torch.bfloat16, (H_kv * d_idx, d_model))
+    _expect("Wk", Wk, torch.bfloat16, (H_kv * d_idx, d_model))
+    _expect("gq", gq, torch.float32, (d_idx,))
+    _expect("gk", gk, torch.float32, (d_idx,))
+    _expect("q_idx", q_idx, torch.bfloat16, (N, H_kv, d_idx))
+    _expect("k_idx", k_idx, torch.bfloat16, (N, H_kv, d_idx))
     dev = hidden.device
     if q_idx is None:
         q_idx = torch.empty((N, H_kv, d_idx), dtype=torch.bfloat16, device=dev)
@@ -306,11 +376,19 @@ def index_kl(Q, K, q_idx, k_idx, lse, row_ptr, col, slot, k, q_start=0, Nq=None,
     """Index-alignment KL(teacher || student) per (query, group) for rows
     [q_start, q_start+Nq): (kl fp32 [Nq, H_kv], kl_sum fp64 [1] or None).
     `lse` is the Main Branch's [Nq, H_q] output for the same rows."""
-    _need_cuda(Q, K, q_idx, k_idx, lse, row_ptr, col, slot)
+    _need_cuda(Q, K, q_idx, k_idx, lse, row_ptr, col, slot, kl, kl_sum)
     Nk, H_kv, d_h = K.shape
     H_q = Q.shape[1]
     d_idx = k_idx.shape[2]
     Nq = Q.shape[0] - q_start if Nq is None else Nq
+    _expect("K", K, torch.bfloat16, (None, H_kv, d_h), q_start + Nq)
+    _expect("Q", Q, torch.bfloat16, (None, H_q, d_h), q_start + Nq)
+    _expect("q_idx", q_idx, torch.bfloat16, (None, H_kv, d_idx), q_start + Nq)
+    _expect("k_idx", k_idx, torch.bfloat16, (None, H_kv, d_idx), Nk)
+    _expect("lse", lse, torch.float32, (Nq, H_q))
+    _expect_csr(row_ptr, col, slot, q_start, Nq, H_kv, k, B_k)
+    _expect("kl", kl, torch.float32, (Nq, H_kv))
+    _expect("kl_sum", kl_sum, torch.float64, (None,), 1)
     scale = 1.0 / math.sqrt(d_h) if scale is None else scale
     lib = load()
     dev = Q.device
@@ -334,9 +412,17 @@ def prefill_workspace_bytes(N, H_q, H_kv, d_h, d_idx, k, chunk=0, B_k=B_K) -> in
 def prefill(Q, K, V, q_idx, k_idx, k, scale=None, chunk=0, B_k=B_K, want_sel=True,
             want_lse=True, sel=None, O=None, lse=None, ws=None):
     """Whole prefill over query chunks: (sel, O, lse)."""
-    _need_cuda(Q, K, V, q_idx, k_idx)
+    _need_cuda(Q, K, V, q_idx, k_idx, sel, O, lse)
     N, H_q, d_h = Q.shape
     H_kv, d_idx = k_idx.shape[1], k_idx.shape[2]
+    _expect("Q", Q, torch.bfloat16, (N, H_q, d_h))
+    _expect("K", K, torch.bfloat16, (N, H_kv, d_h))
+    _expect("V", V, torch.bfloat16, (N, H_kv, d_h))
+    _expect("q_idx", q_idx, torch.bfloat16, (N, H_kv, d_idx))
+    _expect("k_idx", k_idx, torch.bfloat16, (N, H_kv, d_idx))
+    _expect("sel", sel, torch.int32, (N, H_kv, k))
+    _expect("O", O, torch.float32, (N, H_q, d_h))
+    _expect("lse", lse, torch.float32, (N, H_q))
     scale = 1.0 / math.sqrt(d_h) if scale is None else scale
     lib = load()
     dev = Q.device
@@ -355,17 +441,25 @@ def prefill(Q, K, V, q_idx, k_idx, k, scale=None, chunk=0, B_k=B_K, want_sel=Tru
     return sel, O, lse
 
 
-def decode_workspace_bytes(B, N, H_q, H_kv, d_h, k, B_k=B_K) -> int:
-    return load().msa_decode_workspace_bytes(B, N, H_q, H_kv, d_h, B_k, k)
+def decode_workspace_bytes(B, N, H_q, H_kv, d_h, d_idx, k, B_k=B_K) -> int:
+    return load().msa_decode_workspace_bytes(B, N, H_q, H_kv, d_h, d_idx, B_k, k)
 
 
 def decode(q, q_idx, K, V, k_idx, k, scale=None, B_k=B_K, want_lse=True, sel=None,
            O=None, lse=None, ws=None):
     """Decode step for B sequences (query = last cache row): (sel, O, lse)."""
-    _need_cuda(q, q_idx, K, V, k_idx)
+    _need_cuda(q, q_idx, K, V, k_idx, sel, O, lse)
     B, N, H_kv, d_h = K.shape
     H_q = q.shape[1]
     d_idx = k_idx.shape[3]
+    _expect("K", K, torch.bfloat16, (B, N, H_kv, d_h))
+    _expect("V", V, torch.bfloat16, (B, N, H_kv, d_h))
+    _expect("k_idx", k_idx, torch.bfloat16, (B, N, H_kv, d_idx))
+    _expect("q", q, torch.bfloat16, (B, H_q, d_h))
+    _expect("q_idx", q_idx, torch.bfloat16, (B, H_kv, d_idx))
+    _expect("sel", sel, torch.int32, (B, H_kv, k))
+    _expect("O", O, torch.float32, (B, H_q, d_h))
+    _expect("lse", lse, torch.float32, (B, H_q))
     scale = 1.0 / math.sqrt(d_h) if scale is None else scale
     lib = load()
     dev = q.device
@@ -376,7 +470,8 @@ def decode(q, q_idx, K, V, k_idx, k, scale=None, B_k=B_K, want_lse=True, sel=Non
     if lse is None and want_lse:
         lse = torch.empty((B, H_q), dtype=torch.float32, device=dev)
     if ws is None:
-        ws = _workspace(lib.msa_decode_workspace_bytes(B, N, H_q, H_kv, d_h, B_k, k), dev)
+        ws = _workspace(lib.msa_decode_workspace_bytes(B, N, H_q, H_kv, d_h, d_idx, B_k, k),
+                        dev)
     _check(lib.msa_decode(_ptr(q), _ptr(q_idx), _ptr(K), _ptr(V), _ptr(k_idx), B, N, H_q,
                           H_kv, d_h, d_idx, B_k, k, scale, _ptr(sel), _ptr(O), _ptr(lse),
                           _ptr(ws), ws.numel(), _stream(q)))

@@ -270,9 +270,12 @@ msa_status msa_index_kl(const void *Q, const void *K, const void *q_idx, const v
  *   K, V [B, N, H_kv, d_h], k_idx [B, N, H_kv, d_idx] bf16
  *   sel out [B, H_kv, k] int32; O out [B, H_q, d_h] fp32;
  *   lse out [B, H_q] fp32, nullable
+ * Besides the common limits, decode needs H_kv * d_idx to divide 512 (the
+ * index scan reads whole tokens per KiB): other shapes return
+ * MSA_ERR_UNSUPPORTED, and the workspace query returns 0 for them.
  */
 size_t msa_decode_workspace_bytes(int B, int64_t N, int H_q, int H_kv, int d_h,
-                                  int B_k, int k);
+                                  int d_idx, int B_k, int k);
 msa_status msa_decode(const void *q, const void *q_idx, const void *K,
                       const void *V, const void *k_idx, int B, int64_t N,
                       int H_q, int H_kv, int d_h, int d_idx, int B_k, int k,
@@ -307,8 +310,14 @@ msa_status msa_index_frontend(const void *hidden, const void *Wq, const void *Wk
  *     workspace, and msa_prefill runs it once over the whole sequence when
  *     the caller passes sel); 0 = GEMM writes the block scores, a separate
  *     wavefront-per-row Top-k reads them.  Both give identical sel.
- *   MSA_OPT_ATTN_CHUNK: max query positions per KV-outer work item, 1..2048
- *     (section 05 part 2: hot blocks are cut along the query dimension).
+ *   MSA_OPT_ATTN_CHUNK: max query positions per KV-outer work item,
+ *     128..2048, default 1024 (section 05 part 2: hot blocks are cut along
+ *     the query dimension).
+ * Thread safety: the values are atomics.  Every entry point reads them
+ * once, when it starts, and runs the whole call with that snapshot; a
+ * change made while a call runs on another thread takes effect from the
+ * next call.  No *_workspace_bytes result depends on them, so a workspace
+ * sized before a change stays large enough after it.
  * Returns MSA_ERR_INVALID_ARG for an unknown option or value.
  */
 #define MSA_OPT_INDEX_FUSED 1

@@ -41,7 +41,10 @@ def test_workspace_sizes(lib):
         2 * 8192 * 15 * 64 * 128
     assert lib.msa_sparse_attn_fwd_workspace_bytes(0, 8192, 64, 4, 96, 128, 16) == 0
     assert lib.msa_prefill_workspace_bytes(1 << 20, 65536, 64, 4, 128, 64, 128, 16) > 0
-    assert lib.msa_decode_workspace_bytes(32, 1 << 20, 64, 4, 128, 128, 16) > 0
+    assert lib.msa_decode_workspace_bytes(32, 1 << 20, 64, 4, 128, 64, 128, 16) > 0
+    # decode's index scan needs H_kv * d_idx to divide 512
+    assert lib.msa_decode_workspace_bytes(2, 1024, 12, 3, 128, 64, 128, 4) == 0
+    assert lib.msa_decode_workspace_bytes(2, 1024, 64, 8, 128, 128, 128, 4) == 0
 
 
 def _err(lib):
@@ -125,6 +128,18 @@ def test_options(lib):
         msa.set_option(99, 1)
     with pytest.raises(msa.MsaError):
         msa.set_option(msa.OPT_ATTN_CHUNK, 0)
+    with pytest.raises(msa.MsaError):
+        msa.set_option(msa.OPT_ATTN_CHUNK, 127)     # below the smallest work item
+    # workspace sizes do not depend on the item size
+    sizes = []
+    for item in (128, 2048):
+        old_item = msa.get_option(msa.OPT_ATTN_CHUNK)
+        msa.set_option(msa.OPT_ATTN_CHUNK, item)
+        sizes.append((lib.msa_sparse_attn_fwd_workspace_bytes(0, 65536, 64, 4, 128, 128, 16),
+                      lib.msa_index_kl_workspace_bytes(0, 65536, 4, 128, 16),
+                      lib.msa_prefill_workspace_bytes(1 << 20, 65536, 64, 4, 128, 64, 128, 16)))
+        msa.set_option(msa.OPT_ATTN_CHUNK, old_item)
+    assert sizes[0] == sizes[1]
     old = msa.get_option(msa.OPT_ATTN_CHUNK)
     msa.set_option(msa.OPT_ATTN_CHUNK, 512)
     assert msa.get_option(msa.OPT_ATTN_CHUNK) == 512

@@ -18,7 +18,9 @@ from block_sparse_long_idx_amd.synth import bf16_bits, make_prefill_inputs
 
 pytestmark = pytest.mark.gpu
 
-REL_L2, MAX_REL = 1e-2, 2e-2
+# About twice the errors these shapes measure (rel-L2 2.4e-3 for dQ, 1.7e-3
+# for dK and dV), so a precision regression of the bf16 partials fails.
+REL_L2, MAX_REL = 5e-3, 1e-2
 
 
 def say(*a):

@@ -214,6 +214,10 @@ DECODE_CASES = [
     (2, 300, 8, 2, 64, 32, 4),          # fewer blocks than k
     (2, 4096, 64, 4, 128, 64, 16),
     (1, 129, 4, 1, 64, 128, 2),         # local block of one token
+    # G > 16: scores in their own LDS buffer beside K, V and q
+    (2, 3000, 64, 2, 128, 64, 8),       # G = 32
+    (2, 2000, 64, 1, 64, 128, 4),       # G = 64, d_h 64
+    (1, 4100, 64, 1, 128, 64, 16),      # G = 64, d_h 128 (the largest LDS footprint)
 ]
 
 
@@ -236,6 +240,11 @@ def test_decode(oracle_lib, case):
 
 
 # ------------------------------------------------------ full-size workloads
+# Oracle results of the full-size workloads, shared by the two Index Branch
+# variants (the inputs are seeded, so both runs see the same tensors).
+_ORACLE_CACHE = {}
+
+
 def _full_prefill_check(oracle_lib, cfg, n_rows, attn_rows=None):
     say("full prefill", cfg.name, "rows", n_rows)
     t = inputs_for(cfg, device="cuda")
@@ -244,25 +253,31 @@ def _full_prefill_check(oracle_lib, cfg, n_rows, attn_rows=None):
     torch.cuda.synchronize()
     rows = np.array(sample_rows(cfg.N, n_rows))
     rows_t = torch.from_numpy(rows).cuda()
-    k_idx = bf16_bits(t["k_idx"])
-    q_rows = bf16_bits(t["q_idx"][rows_t])
-    say("oracle select", len(rows))
-    sel_ref = oracle_lib.select(q_rows, k_idx, rows, cfg.k)
-    np.testing.assert_array_equal(sel[rows_t].cpu().numpy(), sel_ref)
     arows = rows if attn_rows is None else np.array(sample_rows(cfg.N, attn_rows))
     ar_t = torch.from_numpy(arows).cuda()
-    sel_a = sel_ref if attn_rows is None else \
-        oracle_lib.select(bf16_bits(t["q_idx"][ar_t]), k_idx, arows, cfg.k)
-    say("oracle attend", len(arows))
-    O_ref, lse_ref = oracle_lib.attend(bf16_bits(t["Q"][ar_t]), bf16_bits(t["K"]),
-                                       bf16_bits(t["V"]), sel_a, arows, cfg.scale)
+    key = (cfg.name, n_rows, attn_rows)
+    if key not in _ORACLE_CACHE:
+        k_idx = bf16_bits(t["k_idx"])
+        say("oracle select", len(rows))
+        sel_ref = oracle_lib.select(bf16_bits(t["q_idx"][rows_t]), k_idx, rows, cfg.k)
+        sel_a = sel_ref if attn_rows is None else \
+            oracle_lib.select(bf16_bits(t["q_idx"][ar_t]), k_idx, arows, cfg.k)
+        say("oracle attend", len(arows))
+        O_ref, lse_ref = oracle_lib.attend(bf16_bits(t["Q"][ar_t]), bf16_bits(t["K"]),
+                                           bf16_bits(t["V"]), sel_a, arows, cfg.scale)
+        _ORACLE_CACHE.clear()
+        _ORACLE_CACHE[key] = (sel_ref, O_ref, lse_ref)
+    sel_ref, O_ref, lse_ref = _ORACLE_CACHE[key]
+    np.testing.assert_array_equal(sel[rows_t].cpu().numpy(), sel_ref)
     assert_attn_close(O[ar_t].cpu().numpy(), O_ref, lse[ar_t].cpu().numpy(), lse_ref)
     return t, sel
 
 
+@pytest.mark.slow
 def test_full_8k(oracle_lib, index_variant):
+    """Every row of the 8K workload: selection, inverted index, O and lse."""
     cfg = CONFIGS["8k"]
-    t, sel = _full_prefill_check(oracle_lib, cfg, cfg.N, attn_rows=512)
+    t, sel = _full_prefill_check(oracle_lib, cfg, cfg.N)
     # inverted index of the full selection, bit-exact
     sel_np = sel.cpu().numpy()
     rp, col, slot = oracle_lib.invert(sel_np, 0, cfg.nblk)
@@ -326,7 +341,8 @@ def test_full_decode_1m(oracle_lib):
     sel, O, lse = msa.decode(t["q"], t["q_idx"], t["K"], t["V"], t["k_idx"], cfg.k,
                              scale=cfg.scale)
     torch.cuda.synchronize()
-    for b in (0, 13, 31):
+    sel, O, lse = sel.cpu(), O.cpu(), lse.cpu()
+    for b in range(cfg.batch):
         say("oracle decode seq", b)
         u = {n: bf16_bits(t[n][b]) for n in t}
         s_ref, O_ref, l_ref = oracle_lib.decode_one(u["q"], u["q_idx"], u["K"], u["V"],
