@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "../../include/msa.h"
@@ -668,10 +669,14 @@ size_t msa_decode_workspace_bytes(int B, int64_t N, int H_q, int H_kv, int d_h, 
   return decode_layout(nullptr, B, N, H_q, H_kv, d_h, k).bytes;
 }
 
-msa_status msa_decode(const void* q, const void* q_idx, const void* K, const void* V,
-                      const void* k_idx, int B, int64_t N, int H_q, int H_kv, int d_h, int d_idx,
-                      int B_k, int k, float scale, int32_t* sel, float* O, float* lse, void* ws,
-                      size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+msa_status check_decode(const void* q, const void* q_idx, const void* K, const void* V,
+                        const void* k_idx, int B, int64_t N, int H_q, int H_kv, int d_h,
+                        int d_idx, int B_k, int k, float scale, const int32_t* sel,
+                        const float* O) {
   if (B < 1 || N < 1) return fail(MSA_ERR_INVALID_ARG, "need B >= 1 and N >= 1");
   if (msa_status st = check_common(0, N, H_kv, B_k, k)) return st;
   if (msa_status st = check_attn_shapes(H_q, H_kv, d_h)) return st;
@@ -679,10 +684,18 @@ msa_status msa_decode(const void* q, const void* q_idx, const void* K, const voi
   if (!q || !q_idx || !K || !V || !k_idx || !sel || !O)
     return fail(MSA_ERR_INVALID_ARG, "null q, q_idx, K, V, k_idx, sel or O");
   if (!(scale > 0.f)) return fail(MSA_ERR_INVALID_ARG, "scale must be > 0");
-  const size_t need = decode_layout(nullptr, B, N, H_q, H_kv, d_h, k).bytes;
-  if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  return MSA_OK;
+}
+
+// The decode launches over a validated shape and a large-enough workspace.
+// Every scratch value a kernel reads was written earlier in the same call
+// (pooled scores of the scanned blocks, partials of the selected slots), so
+// the workspace needs no clearing.
+msa_status run_decode(const void* q, const void* q_idx, const void* K, const void* V,
+                      const void* k_idx, int B, int64_t N, int H_q, int H_kv, int d_h, int d_idx,
+                      int k, float scale, int32_t* sel, float* O, float* lse, void* ws,
+                      hipStream_t s) {
   DecodeWs w = decode_layout(ws, B, N, H_q, H_kv, d_h, k);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const int nblk = (int)cdiv(N, kB);
   msa_status st = MSA_OK;
   if (nblk > 1)
@@ -696,9 +709,79 @@ msa_status msa_decode(const void* q, const void* q_idx, const void* K, const voi
                                           w.lse_part, s),
                   "decode attention launch");
   if (st) return st;
-  st = hip_status(msa::launch_decode_merge(w.Opart, w.lse_part, B, H_q, d_h, k,
-                                           std::min(k, nblk), O, lse, s),
-                  "decode merge launch");
+  return hip_status(msa::launch_decode_merge(w.Opart, w.lse_part, B, H_q, d_h, k,
+                                            std::min(k, nblk), O, lse, s),
+                    "decode merge launch");
+}
+
+// Scratch of msa_decode_static: one copy per GPU, resident until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels and copies take the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device
+// with that device current.
+msa_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess)
+    return fail(MSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MSA_ERR_UNSUPPORTED, "device %d is beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess || !p)
+      return fail(MSA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status msa_decode(const void* q, const void* q_idx, const void* K, const void* V,
+                      const void* k_idx, int B, int64_t N, int H_q, int H_kv, int d_h, int d_idx,
+                      int B_k, int k, float scale, int32_t* sel, float* O, float* lse, void* ws,
+                      size_t ws_bytes, void* stream) {
+  if (msa_status st = check_decode(q, q_idx, K, V, k_idx, B, N, H_q, H_kv, d_h, d_idx, B_k, k,
+                                   scale, sel, O))
+    return st;
+  const size_t need = decode_layout(nullptr, B, N, H_q, H_kv, d_h, k).bytes;
+  if (!ws || ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  msa_status st = run_decode(q, q_idx, K, V, k_idx, B, N, H_q, H_kv, d_h, d_idx, k, scale, sel,
+                             O, lse, ws, static_cast<hipStream_t>(stream));
+  return st ? st : ok();
+}
+
+size_t msa_decode_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+msa_status msa_decode_static(const void* q, const void* q_idx, const void* K, const void* V,
+                             const void* k_idx, int B, int64_t N, int H_q, int H_kv, int d_h,
+                             int d_idx, int B_k, int k, float scale, int32_t* sel, float* O,
+                             float* lse, void* stream) {
+  if (msa_status st = check_decode(q, q_idx, K, V, k_idx, B, N, H_q, H_kv, d_h, d_idx, B_k, k,
+                                   scale, sel, O))
+    return st;
+  const size_t need = decode_layout(nullptr, B, N, H_q, H_kv, d_h, k).bytes;
+  if (need > kStaticScratchBytes)
+    return fail(MSA_ERR_WORKSPACE,
+                "decode needs %zu bytes of scratch, more than the fixed %zu of the static "
+                "entry point: use msa_decode with a workspace",
+                need, kStaticScratchBytes);
+  void* ws = nullptr;
+  if (msa_status st = static_scratch(&ws)) return st;
+  msa_status st = run_decode(q, q_idx, K, V, k_idx, B, N, H_q, H_kv, d_h, d_idx, k, scale, sel,
+                             O, lse, ws, static_cast<hipStream_t>(stream));
   return st ? st : ok();
 }
 

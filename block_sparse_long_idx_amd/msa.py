@@ -72,6 +72,9 @@ def load():
         "msa_sparse_attn_bwd_workspace_bytes": ([i64, i64, i32, i32, i32, i32, i32], sz),
         "msa_sparse_attn_bwd": ([P, P, P, P, P, P, P, P, P, i64, i64, i64, i32, i32, i32,
                                  i32, i32, f32, P, P, P, P, sz, P], i32),
+        "msa_decode_static_scratch_bytes": ([], sz),
+        "msa_decode_static": ([P, P, P, P, P, i32, i64, i32, i32, i32, i32, i32, i32, f32, P,
+                               P, P, P], i32),
         "msa_set_option": ([i32, i64], i32),
         "msa_get_option": ([i32], i64),
     }
@@ -443,6 +446,29 @@ def prefill(Q, K, V, q_idx, k_idx, k, scale=None, chunk=0, B_k=B_K, want_sel=Tru
 
 def decode_workspace_bytes(B, N, H_q, H_kv, d_h, d_idx, k, B_k=B_K) -> int:
     return load().msa_decode_workspace_bytes(B, N, H_q, H_kv, d_h, d_idx, B_k, k)
+
+
+def decode_static(q, q_idx, K, V, k_idx, k, sel, O, lse=None, scale=None, B_k=B_K):
+    """Decode step through msa_decode_static: no workspace, no allocation.
+    The caller passes every output (sel int32 [B, H_kv, k], O fp32
+    [B, H_q, d_h], lse fp32 [B, H_q] or None)."""
+    _need_cuda(q, q_idx, K, V, k_idx, sel, O, lse)
+    B, N, H_kv, d_h = K.shape
+    H_q = q.shape[1]
+    d_idx = k_idx.shape[3]
+    _expect("K", K, torch.bfloat16, (B, N, H_kv, d_h))
+    _expect("V", V, torch.bfloat16, (B, N, H_kv, d_h))
+    _expect("k_idx", k_idx, torch.bfloat16, (B, N, H_kv, d_idx))
+    _expect("q", q, torch.bfloat16, (B, H_q, d_h))
+    _expect("q_idx", q_idx, torch.bfloat16, (B, H_kv, d_idx))
+    _expect("sel", sel, torch.int32, (B, H_kv, k))
+    _expect("O", O, torch.float32, (B, H_q, d_h))
+    _expect("lse", lse, torch.float32, (B, H_q))
+    scale = 1.0 / math.sqrt(d_h) if scale is None else scale
+    _check(load().msa_decode_static(_ptr(q), _ptr(q_idx), _ptr(K), _ptr(V), _ptr(k_idx), B, N,
+                                    H_q, H_kv, d_h, d_idx, B_k, k, scale, _ptr(sel), _ptr(O),
+                                    _ptr(lse), _stream(q)))
+    return sel, O, lse
 
 
 def decode(q, q_idx, K, V, k_idx, k, scale=None, B_k=B_K, want_lse=True, sel=None,

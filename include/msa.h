@@ -283,6 +283,29 @@ msa_status msa_decode(const void *q, const void *q_idx, const void *K,
                       size_t ws_bytes, void *stream);
 
 /*
+ * msa_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, kernels and
+ * results as msa_decode; the scratch lives in a fixed device array of
+ * msa_decode_static_scratch_bytes() bytes (64 MiB) that the library holds
+ * on each GPU it runs on until the process ends.  The call allocates and
+ * frees nothing.
+ *   Limit: msa_decode_workspace_bytes() of the shape must not exceed the
+ *   fixed size, else MSA_ERR_WORKSPACE before anything is enqueued (32
+ *   sequences of 1M tokens at H_q 64, H_kv 4, d_h 128, k 16 take 20 MiB).
+ *   Sharing: every call on one GPU uses that GPU's one array.  Calls that
+ *   overlap on one GPU (concurrent streams, or threads enqueueing on
+ *   different streams) race on it; serialise them, e.g. on one stream.
+ *   Nothing in the array needs clearing between calls.
+ */
+size_t msa_decode_static_scratch_bytes(void);
+msa_status msa_decode_static(const void *q, const void *q_idx, const void *K,
+                             const void *V, const void *k_idx, int B, int64_t N,
+                             int H_q, int H_kv, int d_h, int d_idx, int B_k,
+                             int k, float scale, int32_t *sel, float *O,
+                             float *lse, void *stream);
+
+/*
  * Index Branch front-end (Figure 1 caption: the hidden states pass a
  * linear projection and "Norm & RoPE" to give Q^idx and K^idx; section 06:
  * RoPE width 64).  For token i at position pos0 + i and group r, with

@@ -122,6 +122,25 @@ def test_prefill_and_decode_reject(lib):
                           FAKE, 1 << 30, NULL) == msa.ERR_UNSUPPORTED   # G = 65
 
 
+def test_decode_static_limits(lib):
+    """The fixed-scratch decode refuses, on the host, shapes whose decode
+    workspace exceeds its scratch, and bad arguments, before any HIP call."""
+    cap = lib.msa_decode_static_scratch_bytes()
+    assert cap == 64 << 20
+    assert lib.msa_decode_workspace_bytes(32, 1 << 20, 64, 4, 128, 64, 128, 16) <= cap
+    big = (256, 1 << 21, 64, 4, 128, 64, 128, 32)
+    assert lib.msa_decode_workspace_bytes(*big) > cap
+    B, N, H_q, H_kv, d_h, d_idx, B_k, k = big
+    five = (FAKE,) * 5
+    assert lib.msa_decode_static(*five, B, N, H_q, H_kv, d_h, d_idx, B_k, k, 0.1, FAKE, FAKE,
+                                 NULL, NULL) == msa.ERR_WORKSPACE
+    assert "scratch" in _err(lib)
+    assert lib.msa_decode_static(*five, 0, 1024, 8, 4, 128, 64, 128, 4, 0.1, FAKE, FAKE, NULL,
+                                 NULL) == msa.ERR_INVALID_ARG
+    assert lib.msa_decode_static(*five, 2, 1024, 12, 3, 128, 64, 128, 4, 0.1, FAKE, FAKE, NULL,
+                                 NULL) == msa.ERR_UNSUPPORTED
+
+
 def test_options(lib):
     assert msa.get_option(msa.OPT_ATTN_CHUNK) >= 1
     with pytest.raises(msa.MsaError):
