@@ -42,38 +42,52 @@ namespace msa {
 // at most `chunk` positions; with `with_local` (the index KL pass) the
 // whole bucket is.  Item = {bucket, start offset into col, count, 0}.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void bucket_items(int64_t bucket, const int32_t* row_ptr, int nblk,
+__device__ __forceinline__ void bucket_items(int64_t bucket, int32_t rp0, int32_t rp1, int nblk,
                                              int64_t q_start, int64_t Nq, int chunk,
-                                             bool with_local, int32_t& n_loc, int32_t& n_non,
-                                             int32_t& items) {
+                                             bool with_local, int32_t& n_loc, int32_t& n_non) {
   const int b = (int)(bucket % nblk);
-  const int32_t cnt = row_ptr[bucket + 1] - row_ptr[bucket];
+  const int32_t cnt = rp1 - rp0;
   const int64_t lo = max(q_start, (int64_t)b * kBlock);
   const int64_t hi = min(q_start + Nq, (int64_t)(b + 1) * kBlock);
   n_loc = hi > lo && !with_local ? (int32_t)(hi - lo) : 0;
   n_non = cnt - n_loc;
-  items = (n_non + chunk - 1) / chunk;
 }
 
 // Items go out heaviest first -- every full item (exactly `chunk` positions)
 // in bucket order, then the buckets' remainders -- so the work-groups that
 // fetch items last get short ones.  n_items[0] = item count; n_items[1] is
-// the attention kernel's fetch counter, cleared here.
+// the attention kernel's fetch counter, cleared here.  Each thread takes a
+// contiguous run of buckets and reads their row_ptr entries sixteen at a
+// time, so each pass costs a few memory round trips.
 __global__ __launch_bounds__(1024) void build_items_kernel(const int32_t* __restrict__ row_ptr,
                                                            int64_t nb, int nblk, int64_t q_start,
                                                            int64_t Nq, int chunk, bool with_local,
                                                            int4* __restrict__ items,
                                                            int32_t* __restrict__ n_items) {
+  constexpr int RB = 16;
   __shared__ int32_t full[1024], rest[1024];
   const int t = threadIdx.x;
   const int64_t per = ceil_div(nb, 1024);
   const int64_t lo = min(nb, per * t), hi = min(nb, per * (t + 1));
+  // row_ptr[x0 .. x0+RB] of the run's next batch
+  auto batch = [&](int64_t x0, int32_t (&rp)[RB + 1]) {
+#pragma unroll
+    for (int u = 0; u <= RB; ++u) rp[u] = x0 + u <= hi ? row_ptr[x0 + u] : 0;
+  };
   int32_t nf = 0, nr = 0;
-  for (int64_t x = lo; x < hi; ++x) {
-    int32_t n_loc, n_non, it;
-    bucket_items(x, row_ptr, nblk, q_start, Nq, chunk, with_local, n_loc, n_non, it);
-    nf += n_non / chunk;
-    nr += n_non % chunk != 0;
+  for (int64_t x0 = lo; x0 < hi; x0 += RB) {
+    int32_t rp[RB + 1];
+    batch(x0, rp);
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      if (x0 + u < hi) {
+        int32_t n_loc, n_non;
+        bucket_items(x0 + u, rp[u], rp[u + 1], nblk, q_start, Nq, chunk, with_local, n_loc,
+                     n_non);
+        nf += n_non / chunk;
+        nr += n_non % chunk != 0;
+      }
+    }
   }
   full[t] = nf;
   rest[t] = nr;
@@ -87,14 +101,22 @@ __global__ __launch_bounds__(1024) void build_items_kernel(const int32_t* __rest
   }
   const int32_t n_full = full[1023];
   int32_t pf = t ? full[t - 1] : 0, pr = n_full + (t ? rest[t - 1] : 0);
-  for (int64_t x = lo; x < hi; ++x) {
-    int32_t n_loc, n_non, it;
-    bucket_items(x, row_ptr, nblk, q_start, Nq, chunk, with_local, n_loc, n_non, it);
-    const int32_t start = row_ptr[x] + n_loc;
-    int32_t done = 0;
-    for (; done + chunk <= n_non; done += chunk)
-      items[pf++] = make_int4((int)x, start + done, chunk, 0);
-    if (done < n_non) items[pr++] = make_int4((int)x, start + done, n_non - done, 0);
+  for (int64_t x0 = lo; x0 < hi; x0 += RB) {
+    int32_t rp[RB + 1];
+    batch(x0, rp);
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      if (x0 + u < hi) {
+        int32_t n_loc, n_non;
+        bucket_items(x0 + u, rp[u], rp[u + 1], nblk, q_start, Nq, chunk, with_local, n_loc,
+                     n_non);
+        const int32_t start = rp[u] + n_loc;
+        int32_t done = 0;
+        for (; done + chunk <= n_non; done += chunk)
+          items[pf++] = make_int4((int)(x0 + u), start + done, chunk, 0);
+        if (done < n_non) items[pr++] = make_int4((int)(x0 + u), start + done, n_non - done, 0);
+      }
+    }
   }
   if (t == 1023) {
     n_items[0] = n_full + rest[1023];

@@ -3,18 +3,27 @@
 // ("MiniMax Sparse Attention" explainer, section 05 part 2: each KV block
 // gathers the queries that selected it).
 //
-// Deterministic, no ordering atomics: the query range is cut into tiles of
-// kTile positions; (1) per tile and group an LDS histogram over blocks,
-// (2) for every bucket an exclusive scan over tiles plus the bucket totals,
-// (3) an exclusive scan of the totals -> row_ptr, (4) per tile and group a
-// scatter that walks the tile's queries in ascending order with an LDS
-// cursor per block.  Inside a bucket positions therefore come out ascending.
+// A deterministic counting sort in three launches, no ordering atomics.
+// The query range is cut into tiles of kTile positions:
+//   (1) per tile and group, an LDS histogram over blocks -> hist[tile][bucket];
+//   (2) per bucket, an exclusive scan over the tiles (in place), and an
+//       exclusive scan of the bucket totals inside each 256-bucket work-group
+//       -> lp[bucket], plus the work-group's total -> agg[wg];
+//   (3) per tile and group, the cursor of every block is
+//       hist[tile][bucket] + lp[bucket] + (sum of agg before the bucket's
+//       work-group), and one wavefront walks the tile's queries in
+//       ascending order, appending each (query, slot) at its block's cursor.
+//       The tile-0 work-groups also write row_ptr.
+// Inside a bucket, positions therefore come out ascending.  Every global
+// read of a tile's selection rows is issued before the first use, so each
+// launch costs about one memory round trip per work-group.
 #include "common.h"
 #include "msa_internal.h"
 
 namespace msa {
 
-constexpr int kTile = 256;
+constexpr int kTile = 512;    // query positions per tile
+constexpr int kScanWg = 256;  // buckets per scan work-group
 
 // (1) hist[tile][r][b] = number of queries of the tile whose group-r row
 //     selects block b.
@@ -22,100 +31,172 @@ __global__ __launch_bounds__(256) void csr_hist_kernel(const int32_t* __restrict
                                                        int64_t Nq, int H_kv, int k, int nblk,
                                                        int32_t* __restrict__ hist) {
   extern __shared__ int32_t cnt[];
-  const int tile = blockIdx.x, r = blockIdx.y;
-  for (int b = threadIdx.x; b < nblk; b += 256) cnt[b] = 0;
-  __syncthreads();
+  const int tile = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+  for (int b = t; b < nblk; b += 256) cnt[b] = 0;
   const int64_t iq0 = (int64_t)tile * kTile;
-  for (int e = threadIdx.x; e < kTile * k; e += 256) {
-    const int64_t iq = iq0 + e / k;
-    if (iq < Nq) {
-      const int32_t b = sel[(iq * H_kv + r) * k + e % k];
-      if (b >= 0) atomicAdd(&cnt[b], 1);
+  const int n = (int)(min(Nq - iq0, (int64_t)kTile) * k);  // entries of this tile
+  __syncthreads();
+  // entry e = (query e / k, slot e % k); sixteen loads in flight per thread
+  for (int e0 = 0; e0 < n; e0 += 16 * 256) {
+    int32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + 256 * u + t;
+      v[u] = e < n ? sel[((iq0 + e / k) * H_kv + r) * k + e % k] : -1;
     }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (v[u] >= 0) atomicAdd(&cnt[v[u]], 1);
   }
   __syncthreads();
   int32_t* dst = hist + ((int64_t)tile * H_kv + r) * nblk;
-  for (int b = threadIdx.x; b < nblk; b += 256) dst[b] = cnt[b];
+  for (int b = t; b < nblk; b += 256) dst[b] = cnt[b];
 }
 
-// (2) per bucket: exclusive prefix over tiles (in place) and the total.
-__global__ __launch_bounds__(256) void csr_tile_scan_kernel(int32_t* __restrict__ hist,
-                                                            int ntiles, int64_t nb,
-                                                            int32_t* __restrict__ total) {
-  const int64_t bucket = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (bucket >= nb) return;
-  int32_t run = 0;
-  for (int t = 0; t < ntiles; ++t) {
-    const int32_t v = hist[(int64_t)t * nb + bucket];
-    hist[(int64_t)t * nb + bucket] = run;
-    run += v;
-  }
-  total[bucket] = run;
-}
-
-// (3) single work-group exclusive scan: out[x] = sum_{y<x} in[y], out[n] = total.
-__global__ __launch_bounds__(1024) void exclusive_scan_kernel(const int32_t* __restrict__ in,
-                                                              int64_t n,
-                                                              int32_t* __restrict__ out) {
-  __shared__ int32_t part[1024];
+// (2) One thread per bucket: exclusive prefix over the tiles (in place),
+//     then an exclusive scan of the bucket totals across the work-group.
+__global__ __launch_bounds__(kScanWg) void csr_scan_kernel(int32_t* __restrict__ hist,
+                                                           int ntiles, int64_t nb,
+                                                           int32_t* __restrict__ lp,
+                                                           int32_t* __restrict__ agg) {
+  __shared__ int32_t part[kScanWg];
   const int t = threadIdx.x;
-  const int64_t per = ceil_div(n, 1024);
-  const int64_t lo = min(n, per * t), hi = min(n, per * (t + 1));
-  int32_t s = 0;
-  for (int64_t x = lo; x < hi; ++x) s += in[x];
-  part[t] = s;
+  const int64_t x = (int64_t)blockIdx.x * kScanWg + t;
+  int32_t run = 0;
+  if (x < nb) {
+    for (int t0 = 0; t0 < ntiles; t0 += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = t0 + u < ntiles ? hist[(int64_t)(t0 + u) * nb + x] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (t0 + u < ntiles) hist[(int64_t)(t0 + u) * nb + x] = run;
+        run += v[u];
+      }
+    }
+  }
+  part[t] = run;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
+  for (int o = 1; o < kScanWg; o <<= 1) {  // Hillis-Steele inclusive scan
     const int32_t v = t >= o ? part[t - o] : 0;
     __syncthreads();
     part[t] += v;
     __syncthreads();
   }
-  int32_t run = t ? part[t - 1] : 0;
-  for (int64_t x = lo; x < hi; ++x) {
-    const int32_t v = in[x];
-    out[x] = run;
-    run += v;
-  }
-  if (t == 1023) out[n] = part[1023];
+  if (x < nb) lp[x] = t ? part[t - 1] : 0;
+  if (t == kScanWg - 1) agg[blockIdx.x] = part[kScanWg - 1];
 }
 
-// (4) scatter: one wavefront per (tile, group).  Lane s handles slot s of
-//     the current query; the k blocks of one query are distinct, so the
-//     lanes never touch the same cursor, and queries are walked in order.
-__global__ __launch_bounds__(64) void csr_scatter_kernel(const int32_t* __restrict__ sel,
-                                                         int64_t q_start, int64_t Nq, int H_kv,
-                                                         int k, int nblk,
-                                                         const int32_t* __restrict__ hist,
-                                                         const int32_t* __restrict__ row_ptr,
-                                                         int32_t* __restrict__ col,
-                                                         uint8_t* __restrict__ slot) {
-  extern __shared__ int32_t cur[];
-  const int tile = blockIdx.x, r = blockIdx.y, lane = threadIdx.x;
-  const int32_t* hb = hist + ((int64_t)tile * H_kv + r) * nblk;
-  const int32_t* rp = row_ptr + (int64_t)r * nblk;
-  for (int b = lane; b < nblk; b += 64) cur[b] = hb[b] + rp[b];
-  __syncthreads();
+// (3) Scatter, work-group per (tile, group r).  LDS: the block cursors, the
+//     exclusive prefix of the scan work-groups' totals and the tile's
+//     selection rows of group r.
+__global__ __launch_bounds__(256) void csr_scatter_kernel(
+    const int32_t* __restrict__ sel, int64_t q_start, int64_t Nq, int H_kv, int k, int nblk,
+    const int32_t* __restrict__ hist, const int32_t* __restrict__ lp,
+    const int32_t* __restrict__ agg, int nwg, int32_t* __restrict__ row_ptr,
+    int32_t* __restrict__ col, uint8_t* __restrict__ slot) {
+  extern __shared__ int32_t smem[];
+  int32_t* cur = smem;               // [nblk + 1]: the last one absorbs padding
+  int32_t* aggp = cur + nblk + 1;    // [nwg + 1]
+  int32_t* selt = aggp + nwg + 1;    // [kTile][k]
+  const int tile = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
   const int64_t iq0 = (int64_t)tile * kTile;
-  const int64_t iq1 = min(Nq, iq0 + kTile);
-  for (int64_t iq = iq0; iq < iq1; ++iq) {
-    if (lane < k) {
-      const int32_t b = sel[(iq * H_kv + r) * k + lane];
-      if (b >= 0) {
-        const int32_t pos = cur[b];
-        cur[b] = pos + 1;
-        col[pos] = (int32_t)(q_start + iq);
-        slot[pos] = (uint8_t)lane;
+  const int nq = (int)min(Nq - iq0, (int64_t)kTile);
+  const int n = nq * k;
+  // the tile's selection rows of group r, all loads in flight
+  for (int e0 = 0; e0 < n; e0 += 16 * 256) {
+    int32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + 256 * u + t;
+      v[u] = e < n ? sel[((iq0 + e / k) * H_kv + r) * k + e % k] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + 256 * u + t;
+      if (e < n) selt[e] = v[u];
+    }
+  }
+  // exclusive prefix of agg: per-thread sums of consecutive runs, then a
+  // scan of the 256 run sums
+  {
+    const int per = (nwg + 255) / 256;
+    const int lo = min(nwg, per * t), hi = min(nwg, per * (t + 1));
+    int32_t s = 0;
+    for (int w = lo; w < hi; ++w) s += agg[w];
+    aggp[nwg] = 0;
+    __shared__ int32_t part[256];
+    part[t] = s;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int32_t v = t >= o ? part[t - o] : 0;
+      __syncthreads();
+      part[t] += v;
+      __syncthreads();
+    }
+    int32_t run = t ? part[t - 1] : 0;
+    for (int w = lo; w < hi; ++w) {
+      aggp[w] = run;
+      run += agg[w];
+    }
+    if (t == 255) aggp[nwg] = part[255];
+  }
+  __syncthreads();
+  const int32_t* hrow = hist + ((int64_t)tile * H_kv + r) * nblk;
+  const int64_t x0 = (int64_t)r * nblk;
+  // the cursors: eight blocks per thread per batch, every load issued first
+  for (int b0 = 0; b0 < nblk; b0 += 8 * 256) {
+    int32_t hv[8], lv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = b0 + 256 * u + t;
+      hv[u] = b < nblk ? hrow[b] : 0;
+      lv[u] = b < nblk ? lp[x0 + b] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = b0 + 256 * u + t;
+      if (b < nblk) {
+        const int32_t start = lv[u] + aggp[(x0 + b) / kScanWg];
+        cur[b] = hv[u] + start;
+        if (tile == 0) row_ptr[x0 + b] = start;
       }
     }
-    __builtin_amdgcn_wave_barrier();
+  }
+  if (tile == 0 && r == H_kv - 1 && t == 0) row_ptr[(int64_t)H_kv * nblk] = aggp[nwg];
+  __syncthreads();
+  if (t >= k) return;
+  // Lanes 0..k-1 of the first wavefront walk the tile's queries in order;
+  // lane s takes slot s (the k blocks of one query are distinct, so the
+  // lanes of one instruction never share a cursor).  Each query's cursor
+  // updates are one LDS atomic add with return, and the LDS executes one
+  // wavefront's instructions in issue order, so eight queries' updates go
+  // out back to back and still take their positions in query order.
+  // Padding entries (-1) and rows past the tile add to the spare cursor
+  // cur[nblk], so no atomic sits behind a branch.
+  if (t == 0) cur[nblk] = 0;
+  for (int iq = 0; iq < nq; iq += 8) {
+    int32_t b[8], pos[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) b[u] = iq + u < nq ? selt[(iq + u) * k + t] : -1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pos[u] = atomicAdd(&cur[b[u] >= 0 ? b[u] : nblk], 1);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (b[u] >= 0) {
+        col[pos[u]] = (int32_t)(q_start + iq0 + iq + u);
+        slot[pos[u]] = (uint8_t)t;
+      }
+    }
   }
 }
+
+static int64_t scan_wgs(int64_t nb) { return ceil_div(nb, kScanWg); }
 
 size_t invert_scratch_bytes(int64_t Nq, int H_kv, int nblk) {
   const int64_t ntiles = ceil_div(Nq, kTile);
   const int64_t nb = (int64_t)H_kv * nblk;
-  return sizeof(int32_t) * (size_t)(ntiles * nb + nb);
+  return sizeof(int32_t) * (size_t)(ntiles * nb + nb + scan_wgs(nb));
 }
 
 hipError_t launch_invert(const int32_t* sel, int64_t q_start, int64_t Nq, int H_kv, int k,
@@ -123,14 +204,26 @@ hipError_t launch_invert(const int32_t* sel, int64_t q_start, int64_t Nq, int H_
                          void* scratch, hipStream_t stream) {
   const int ntiles = (int)ceil_div(Nq, kTile);
   const int64_t nb = (int64_t)H_kv * nblk;
+  const int nwg = (int)scan_wgs(nb);
   int32_t* hist = static_cast<int32_t*>(scratch);
-  int32_t* total = hist + (int64_t)ntiles * nb;
-  const size_t lds = sizeof(int32_t) * (size_t)nblk;
-  csr_hist_kernel<<<dim3(ntiles, H_kv), 256, lds, stream>>>(sel, Nq, H_kv, k, nblk, hist);
-  csr_tile_scan_kernel<<<(unsigned)ceil_div(nb, 256), 256, 0, stream>>>(hist, ntiles, nb, total);
-  exclusive_scan_kernel<<<1, 1024, 0, stream>>>(total, nb, row_ptr);
-  csr_scatter_kernel<<<dim3(ntiles, H_kv), 64, lds, stream>>>(sel, q_start, Nq, H_kv, k, nblk,
-                                                               hist, row_ptr, col, slot);
+  int32_t* lp = hist + (int64_t)ntiles * nb;
+  int32_t* agg = lp + nb;
+  // scatter LDS: nblk + 1 + nwg + 1 + kTile * k ints, at most 16385 + 4097
+  // + 16384 (H_kv <= 64, nblk <= 16384, k <= 32): 144 KiB
+  const size_t lds_hist = sizeof(int32_t) * (size_t)nblk;
+  const size_t lds_scatter = sizeof(int32_t) * ((size_t)nblk + 1 + nwg + 1 + (size_t)kTile * k);
+  static bool lds_ready = false;
+  if (!lds_ready) {
+    const int most = (int)(sizeof(int32_t) * (16385 + 4097 + kTile * 32));
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&csr_scatter_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, most);
+    if (e != hipSuccess) return e;
+    lds_ready = true;
+  }
+  csr_hist_kernel<<<dim3(ntiles, H_kv), 256, lds_hist, stream>>>(sel, Nq, H_kv, k, nblk, hist);
+  csr_scan_kernel<<<(unsigned)nwg, kScanWg, 0, stream>>>(hist, ntiles, nb, lp, agg);
+  csr_scatter_kernel<<<dim3(ntiles, H_kv), 256, lds_scatter, stream>>>(
+      sel, q_start, Nq, H_kv, k, nblk, hist, lp, agg, nwg, row_ptr, col, slot);
   return hipGetLastError();
 }
 

@@ -146,34 +146,50 @@ __device__ __forceinline__ void index_sweep(const __bf16* __restrict__ q_idx,
             }
         }
       } else {
-        // one key-row group at a time: each LDS fragment feeds CG MFMAs
+        // Key-row group g, k-step s in sequence: each LDS fragment feeds CG
+        // MFMAs, and the next fragment is read while they run (one
+        // fragment ahead, so its LDS latency hides under CG MFMAs and only
+        // two fragments are live).
+        auto frag = [&](int st) {
+          const int row = 32 * (st / S) + n;
+          return *reinterpret_cast<const bf16x8*>(
+              &lds[buf][row * D + 8 * (((D / 16) * h + st % S) ^ kswz<D>(row))]);
+        };
+        f32x16 acc[CG];
+        bf16x8 a_cur = frag(0);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int row = 32 * g + n;
-          bf16x8 a[S];
+        for (int st = 0; st < 4 * S; ++st) {
+          const int s = st % S;
+          const bf16x8 a_nxt = st + 1 < 4 * S ? frag(st + 1) : a_cur;
+          if (s == 0) {
 #pragma unroll
-          for (int s = 0; s < S; ++s)
-            a[s] = *reinterpret_cast<const bf16x8*>(
-                &lds[buf][row * D + 8 * (((D / 16) * h + s) ^ kswz<D>(row))]);
-          f32x16 acc[CG];
+            for (int c = 0; c < CG; ++c) acc[c] = f32x16{};
+          }
 #pragma unroll
-          for (int c = 0; c < CG; ++c) acc[c] = f32x16{};
+          for (int c = 0; c < CG; ++c) acc[c] = mfma32(a_cur, qb[c][s], acc[c]);
+          if (st == 0 && kb_prev >= 0) sink(kb_prev, kb_end_w, v_prev);
+          if (s == S - 1) {
 #pragma unroll
-          for (int s = 0; s < S; ++s)
+            for (int c = 0; c < CG; ++c)
 #pragma unroll
-            for (int c = 0; c < CG; ++c) acc[c] = mfma32(a[s], qb[c][s], acc[c]);
-          if (g == 0 && kb_prev >= 0) sink(kb_prev, kb_end_w, v_prev);
-#pragma unroll
-          for (int c = 0; c < CG; ++c)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) m[c] = fmaxf(m[c], acc[c][j]);
+              for (int j = 0; j < 16; ++j) m[c] = fmaxf(m[c], acc[c][j]);
+          }
+          a_cur = a_nxt;
         }
       }
-#pragma unroll
-      for (int c = 0; c < CG; ++c) m[c] = fmaxf(m[c], __shfl_xor(m[c], 32, kWave));
       kb_prev = kb;
+      // Lane half h keeps column groups 2j+h: it sends across its partial
+      // max of the other group of each pair and takes the other half's
+      // partial max of its own.  The selects are bit operations on a lane
+      // mask, which keeps the hand-over in registers.
+      const uint32_t hm = h ? 0xffffffffu : 0u;
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) v_prev[j] = h ? m[2 * j + 1] : m[2 * j];
+      for (int j = 0; j < NQ; ++j) {
+        const uint32_t a = __float_as_uint(m[2 * j]), b = __float_as_uint(m[2 * j + 1]);
+        const float mine = __uint_as_float((b & hm) | (a & ~hm));
+        const float other = __uint_as_float((a & hm) | (b & ~hm));
+        v_prev[j] = fmaxf(mine, __shfl_xor(other, 32, kWave));
+      }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of block kb+1 is in LDS
     __syncthreads();
@@ -247,26 +263,38 @@ __global__ __launch_bounds__(64 * NW) void index_pool_kernel(
 // query, sorted by score, descending.  Blocks arrive in ascending order and
 // a new score must beat an equal one strictly, so among equal scores the
 // lower block stays ahead (ties go to the lower block index).
+// Inserting v moves every entry it beats one place down: the new score at
+// place j is the median of (old j-1, v, old j), since the list is sorted;
+// the block ids follow the same two comparisons.  Places 0..LM/2 can only
+// change when v beats the entry at LM/2, so that half is skipped (by the
+// whole wave) when no lane's v reaches it: late in the sweep most new
+// entries land near the bottom of the list.
 template <int LM, int NQ>
 struct TopkKeep {
   int lb_own[NQ];
   float sc[NQ][LM];
   int bk[NQ][LM];
+  __device__ __forceinline__ void place(int q, int j, float v, int kb) {
+    const bool up = v > sc[q][j - 1];
+    const bool here = v > sc[q][j];
+    bk[q][j] = up ? bk[q][j - 1] : (here ? kb : bk[q][j]);
+    sc[q][j] = __builtin_amdgcn_fmed3f(sc[q][j - 1], v, sc[q][j]);
+  }
   __device__ __forceinline__ void operator()(int kb, int, const float (&vin)[NQ]) {
+    constexpr int SP = LM / 2;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       // A block that must not enter (the local block or later) becomes -inf.
       const float v = kb < lb_own[q] ? vin[q] : -INFINITY;
       if (v > sc[q][LM - 1]) {
 #pragma unroll
-        for (int j = LM - 1; j > 0; --j) {
-          const bool up = v > sc[q][j - 1];
-          const bool here = v > sc[q][j];
-          sc[q][j] = up ? sc[q][j - 1] : (here ? v : sc[q][j]);
-          bk[q][j] = up ? bk[q][j - 1] : (here ? kb : bk[q][j]);
+        for (int j = LM - 1; j > SP; --j) place(q, j, v, kb);
+        if (v > sc[q][SP]) {
+#pragma unroll
+          for (int j = SP; j > 0; --j) place(q, j, v, kb);
+          bk[q][0] = v > sc[q][0] ? kb : bk[q][0];
+          sc[q][0] = fmaxf(v, sc[q][0]);
         }
-        bk[q][0] = v > sc[q][0] ? kb : bk[q][0];
-        sc[q][0] = v > sc[q][0] ? v : sc[q][0];
       }
     }
   }
