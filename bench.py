@@ -411,10 +411,24 @@ def cpu_baseline(cfg, t, n_rows):
     sel = oracle.select(q_rows, k_idx, rows, cfg.k, nthreads=nthreads)
     oracle.attend(Q_rows, K, V, sel, rows, cfg.scale, nthreads=nthreads)
     dt = time.perf_counter() - t0
+
+    # Extrapolation to every row of the sequence by the oracle's own cost per
+    # row: selection scores i+1 keys per group (d_idx multiply-adds each),
+    # attention touches min(k*B_k, i+1) keys per head (2 d_h each).
+    def row_cost(i):
+        i = np.asarray(i, dtype=np.float64)
+        return (i + 1) * cfg.d_idx * cfg.H_kv + \
+            np.minimum(cfg.k * cfg.B_k, i + 1) * 2 * cfg.d_h * cfg.H_q
+
+    full_s = dt * float(row_cost(np.arange(cfg.N)).sum()) / float(row_cost(rows).sum())
     return {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": nthreads,
             "kind": "oracle",
             "sample": f"{len(rows)} query rows evenly spaced over positions 0..{cfg.N - 1} "
-                      f"of the same workload (all heads and groups), {dt:.1f} s wall"}
+                      f"of the same workload (all heads and groups), {dt:.1f} s wall",
+            "extrapolated_all_rows_s": round(full_s, 1),
+            "extrapolation": "sample wall time scaled by the oracle's per-row work "
+                             "(i+1 index scores per group + min(k*B_k, i+1) keys per head) "
+                             "summed over all N rows vs the sampled rows"}
 
 
 def time_decode(cfg, steps, warmup):
