@@ -554,6 +554,20 @@ def main():
                  "unit": "GB/s", "frac": round(main_gbs / PEAK_HBM_GBS, 4),
                  "algorithmic_bytes_per_step": main_bytes}
 
+    # The inverted index against HBM: per chunk the selection table is read
+    # (4 B per (query, group, slot)), col and slot written (5 B per entry)
+    # and row_ptr written (4 B per bucket).
+    inv_bytes = 0
+    for q0, nq in chunks_of(cfg):
+        nblk_c = -(-(q0 + nq) // cfg.B_k)
+        inv_bytes += 4 * nq * cfg.H_kv * cfg.k + 5 * msa.selection_nnz(q0, nq, cfg.H_kv, cfg.k) \
+            + 4 * (cfg.H_kv * nblk_c + 1)
+    inv_gbs = inv_bytes / (stages[1] / 1e3) / 1e9
+    roof_inv = {"stage": "invert_index", "kernels": "csr_hist_kernel, csr_scan_kernel, "
+                "csr_scatter_kernel per query chunk", "bound": "hbm",
+                "achieved": round(inv_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(inv_gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_step": inv_bytes}
+
     out = {
         "metric": "MSA prefill tokens/s + effective TFLOP/s (% bf16 MFMA peak) at 128K and 1M",
         "value": round(cfg.N / (ms / 1e3), 1),
@@ -575,6 +589,7 @@ def main():
         "stage_ms": {n: round(s, 3) for n, s in zip(stage_names, stages)},
         "roofline": roof,
         "roofline_main_branch": roof_main,
+        "roofline_invert_index": roof_inv,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on {args.cpu_rows} sampled rows")
