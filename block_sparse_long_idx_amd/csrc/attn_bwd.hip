@@ -56,6 +56,23 @@ __device__ __forceinline__ bf16x8 tr_frag(const __bf16* t, int d, int c0, int h)
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// The transposed [d][row] Q and dO tiles swap 8-row halves of a d row by
+// d / 32: the staging stores (lanes spread over 16 d-chunks of 8 d at two
+// rows each) then hit distinct banks instead of piling 4-8 lanes onto one,
+// while the fragment reads keep their 4-row runs contiguous and stay
+// conflict-free.  Measured: LDS bank-conflict cycles 3.7e9 -> 0.53e9 per
+// 128K backward, 50.8 -> 45.1 ms, bitwise identical gradients.
+__device__ __forceinline__ int tsw(int d) { return ((d >> 5) & 3) << 3; }
+
+// Fragment of a transposed Q / dO tile: row d, tile rows c0 + 4h .. and
+// c0 + 8 + 4h .. (tr_frag's order), through the swizzle.
+__device__ __forceinline__ bf16x8 qt_frag(const __bf16* t, int d, int c0, int h) {
+  const int sw = tsw(d);
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&t[d * kRp + ((c0 + 4 * h) ^ sw)]);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&t[d * kRp + ((c0 + 8 + 4 * h) ^ sw)]);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 }  // namespace
 
 int bwd_unit_positions(int G) { return std::min(kUnitPos, std::max(1, kUnitRows / G)); }
@@ -304,7 +321,8 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<bf16x2*>(&tr[(8 * c + e) * kRp + 2 * rp]) = bf16x2{y[0][e], y[1][e]};
+          *reinterpret_cast<bf16x2*>(&tr[(8 * c + e) * kRp + ((2 * rp) ^ tsw(8 * c + e))]) =
+              bf16x2{y[0][e], y[1][e]};
       }
       if (tl < 32) {
         sm.lim[b2][tl] = mlim;
@@ -328,9 +346,9 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             av[i] = mfma32(tr_frag<kRp>(sm.pt[b2], kw + nn, 16 * u, h),
-                           tr_frag<kRp>(sm.gt[b3], 32 * dg + nn, 16 * u, h), av[i]);
+                           qt_frag(sm.gt[b3], 32 * dg + nn, 16 * u, h), av[i]);
             ak[i] = mfma32(tr_frag<kRp>(sm.dst[b2], kw + nn, 16 * u, h),
-                           tr_frag<kRp>(sm.qt[b3], 32 * dg + nn, 16 * u, h), ak[i]);
+                           qt_frag(sm.qt[b3], 32 * dg + nn, 16 * u, h), ak[i]);
           }
         }
         if (kw < DH) {
@@ -393,8 +411,8 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
         for (int i = 0; i < NDH; ++i) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            av[i] = mfma32(pA[u], tr_frag<kRp>(sm.gt[b3], 32 * i + nn, 16 * u, h), av[i]);
-            ak[i] = mfma32(dA[u], tr_frag<kRp>(sm.qt[b3], 32 * i + nn, 16 * u, h), ak[i]);
+            av[i] = mfma32(pA[u], qt_frag(sm.gt[b3], 32 * i + nn, 16 * u, h), av[i]);
+            ak[i] = mfma32(dA[u], qt_frag(sm.qt[b3], 32 * i + nn, 16 * u, h), ak[i]);
           }
         }
         // dS [row][key] for dQ; P^T and dS^T [key][row] for the consumers:
