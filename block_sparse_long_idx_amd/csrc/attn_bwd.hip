@@ -10,19 +10,19 @@
 //   dQ = scale * sum_j ds_j K_j,  dK_j += scale * ds_j Q,  dV_j += p_j dO
 // One KV-outer pass over the forward's inverted index (local positions
 // included, with the causal mask).  A work unit is one bucket (group r,
-// block b), or a fixed-size slice of a large one.  Its work-group keeps the
-// block's K and V in registers (each of the four waves owns 32 keys) and
-// sweeps the unit's rows -- (position, head) pairs -- in 32-row tiles that
-// are double-buffered in LDS, row-major for S = Q K^T and dP = dO V^T and
-// transposed for dV += P^T dO and dK += dS^T Q (the contractions over
-// rows).  Each tile's dS goes through LDS so that the waves, now owning 32
-// d each, form dQ^T = K^T dS^T over all 128 keys; that is stored as a bf16
+// block b), or a fixed-size slice of a large one.  Its work-group keeps
+// the block's K and V in registers (each 32-key slice on its own waves)
+// and sweeps the unit's rows -- (position, head) pairs -- in 32-row tiles
+// staged row-major in LDS: S = Q K^T and dP = dO V^T read them as plain
+// fragments, dV += P^T dO and dK += dS^T Q (the contractions over rows)
+// through the transpose read, so no transposed copy is made.  Each tile's
+// dS^T goes through LDS so that the waves, now owning 32 d each, form
+// dQ^T = K^T dS^T over all 128 keys; that is stored as a bf16
 // partial per (i, h, slot) and summed per (i, h) in ascending slot order by
 // a second kernel.  A whole bucket adds its dK/dV sums to the outputs at
 // the end; the slices of a split bucket write fp32 partials that a third
 // kernel sums in slice order.  Deterministic, no atomics on the outputs.
 #include "common.h"
-#include "lds_rows.h"
 #include "msa_internal.h"
 
 #include <algorithm>
@@ -32,44 +32,76 @@ namespace msa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kRp = 32 + 4;       // pitch of a transposed [d][32 rows] tile
-constexpr int kDsp = kBlock + 4;  // pitch of the [32 rows][128 keys] dS tile
 constexpr int kUnitRows = 16384;  // rows per work unit, at most
 constexpr int kUnitPos = 1024;    // positions per work unit, at most
 
-// A fragment (MFMA A or B: 32 rows x 16 d at k-step s) of a row-major
-// swizzled tile; lane half h covers d in [h*D/2, (h+1)*D/2).
+// The Q and dO rows of a 32-row tile sit row-major in LDS, their 16-byte
+// chunks XOR-swizzled by qsw(row).  Two kinds of read hit them: a fragment
+// read (16 lanes on 16 consecutive rows, one chunk each) and a transpose
+// read (each 16-lane group on 4 consecutive rows, 32 bytes of each).  For
+// d = 128 a row spans all 64 banks and qsw spreads the low two row bits
+// over the chunk index's high bits and the next two over its low bits, so
+// both kinds land on distinct banks; for d = 64 two rows share a bank row.
 template <int D>
-__device__ __forceinline__ bf16x8 rm_frag(const __bf16* blk, int row, int s, int h) {
-  return *reinterpret_cast<const bf16x8*>(
-      &blk[row * D + 8 * (((D / 16) * h + s) ^ row_swz<D>(row))]);
+__device__ __forceinline__ int qsw(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                  : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int qoff(int row, int col) {
+  return row * D + 8 * ((col >> 3) ^ qsw<D>(row)) + (col & 7);
 }
 
-// Fragment with the contraction over 16 entries c0.. of a row of t[.][PITCH]:
-// lane half h takes entries c0 + 4h + {0..3} and c0 + 8 + 4h + {0..3}, which
-// is the order in which an accumulator's registers 8u..8u+7 hold rows 16u..
-// (so an accumulator can be the other operand).
-template <int PITCH>
-__device__ __forceinline__ bf16x8 tr_frag(const __bf16* t, int d, int c0, int h) {
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&t[d * PITCH + c0 + 4 * h]);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&t[d * PITCH + c0 + 8 + 4 * h]);
+// MFMA A/B fragment of a row tile: 32 rows x 16 d at k-step s, lane half h
+// covering d in [h*D/2, (h+1)*D/2).
+template <int D>
+__device__ __forceinline__ bf16x8 qr_frag(const __bf16* blk, int row, int s, int h) {
+  return *reinterpret_cast<const bf16x8*>(&blk[row * D + 8 * (((D / 16) * h + s) ^ qsw<D>(row))]);
+}
+
+typedef __bf16 bf16v4 __attribute__((ext_vector_type(4)));
+
+// LDS transpose read (gfx950): in each group of 16 lanes, lane m reads 4
+// consecutive 16-bit values at its own address, and lane i receives, as
+// its value j, value i%4 of lane 4j + i/4.  So if the group's lanes read a
+// 4-row x 16-column block row by row (lane m: row m/4, columns 4(m%4)..),
+// each lane ends up holding its own column over the 4 rows.
+__device__ __forceinline__ bf16x4 ld_tr(const __bf16* p) {
+  const bf16v4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (bf16v4 __attribute__((address_space(3)))*)p);
+  return bf16x4{v[0], v[1], v[2], v[3]};
+}
+
+// Operand with the contraction over tile rows c0..c0+15 of a row tile:
+// lane (n, h) gets column d0 + n at rows c0 + 4h + {0..3} and
+// c0 + 8 + 4h + {0..3}, the order in which an accumulator's registers
+// 8u..8u+7 hold rows 16u.. (so an accumulator can be the other operand).
+template <int D>
+__device__ __forceinline__ bf16x8 qtr_frag(const __bf16* blk, int d0, int c0, int h, int n) {
+  const int row = c0 + 4 * h + ((n >> 2) & 3), col = d0 + (n & 16) + 4 * (n & 3);
+  const bf16x4 lo = ld_tr(blk + qoff<D>(row, col));
+  const bf16x4 hi = ld_tr(blk + qoff<D>(row + 8, col));
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// The transposed [d][row] Q and dO tiles swap 8-row halves of a d row by
-// d / 32: the staging stores (lanes spread over 16 d-chunks of 8 d at two
-// rows each) then hit distinct banks instead of piling 4-8 lanes onto one,
-// while the fragment reads keep their 4-row runs contiguous and stay
-// conflict-free.  Measured: LDS bank-conflict cycles 3.7e9 -> 0.53e9 per
-// 128K backward, 50.8 -> 45.1 ms, bitwise identical gradients.
-__device__ __forceinline__ int tsw(int d) { return ((d >> 5) & 3) << 3; }
-
-// Fragment of a transposed Q / dO tile: row d, tile rows c0 + 4h .. and
-// c0 + 8 + 4h .. (tr_frag's order), through the swizzle.
-__device__ __forceinline__ bf16x8 qt_frag(const __bf16* t, int d, int c0, int h) {
-  const int sw = tsw(d);
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&t[d * kRp + ((c0 + 4 * h) ^ sw)]);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&t[d * kRp + ((c0 + 8 + 4 * h) ^ sw)]);
+// P^T and dS^T tiles [key][32 rows]: 8-byte pieces (4 rows) XOR-swizzled
+// by key, so that 32 keys storing one piece each, 32 keys reading their
+// rows and a transpose read over 4 keys x 32 rows all hit distinct banks.
+__device__ __forceinline__ int koff(int key, int row) {
+  return key * 32 + 4 * ((row >> 2) ^ ((key >> 2) & 7)) + (row & 3);
+}
+// Operand holding key `key` at tile rows c0 + 4h + {0..3}, c0 + 8 + 4h + {0..3}.
+__device__ __forceinline__ bf16x8 kt_frag(const __bf16* t, int key, int c0, int h) {
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&t[koff(key, c0 + 4 * h)]);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&t[koff(key, c0 + 8 + 4 * h)]);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// Operand with the contraction over keys c0..c0+15: lane (n, h) gets tile
+// row n at keys c0 + 4h + {0..3} and c0 + 8 + 4h + {0..3} (transpose read).
+__device__ __forceinline__ bf16x8 ktr_frag(const __bf16* t, int c0, int h, int n) {
+  const int key = c0 + 4 * h + ((n >> 2) & 3), row = (n & 16) + 4 * (n & 3);
+  const bf16x4 lo = ld_tr(t + koff(key, row));
+  const bf16x4 hi = ld_tr(t + koff(key + 8, row));
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -162,13 +194,10 @@ __global__ __launch_bounds__(1024) void build_bwd_units_kernel(
 
 template <int DH>
 struct BwdSmem {
-  __bf16 qr[2][32 * DH];    // the tile's Q rows, row-major swizzled
-  __bf16 gr[2][32 * DH];    // the tile's dO rows
-  __bf16 qt[3][DH * kRp];   // the same, transposed [d][row] (three tiles live)
-  __bf16 gt[3][DH * kRp];
-  __bf16 ds[2][32 * kDsp];  // dS [row][key], for dQ
-  __bf16 pt[2][kBlock * kRp];   // P^T [key][row], for the second d-half's dV
-  __bf16 dst[2][kBlock * kRp];  // dS^T [key][row], for its dK
+  __bf16 qr[3][32 * DH];         // the tile's Q rows, row-major swizzled (three tiles live)
+  __bf16 gr[3][32 * DH];         // the tile's dO rows
+  __bf16 pt[2][kBlock * 32];     // P^T [key][row], for the second d-half's dV
+  __bf16 dst[2][kBlock * 32];    // dS^T [key][row], for its dK and for dQ
   int32_t lim[2][32];       // per tile row: last visible key of the block (-1: none)
   float l2[2][32];          // lse * log2(e)
   float dv[2][32];          // D = dO . O
@@ -176,13 +205,11 @@ struct BwdSmem {
   uint8_t sl[kUnitPos];     // and the block's slot in each one's selection
 };
 
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-
 // Eight waves per work-group, two per SIMD, in producer/consumer pairs
 // over the same 32 keys kw = 32 (w mod 4):
 //  - waves 0-3 (first d-half) form S = Q K^T and dP = dO V^T, the softmax
 //    and dS for tile T, add its P^T dO and dS^T Q into dV/dK for d < DH/2,
-//    and leave dS, P^T and dS^T in LDS;
+//    and leave P^T and dS^T in LDS;
 //  - waves 4-7 take tile T-1 from LDS after the barrier: dV/dK for the
 //    second d-half, and dQ^T = K^T dS^T for their 32-wide d-slice (K^T in
 //    registers).
@@ -309,20 +336,15 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
     auto store = [&](int T) {
       const int b2 = T & 1, b3 = T % 3;
       if (which < 2) {
-        __bf16* rm = which == 0 ? sm.qr[b2] : sm.gr[b2];
-        __bf16* tr = which == 0 ? sm.qt[b3] : sm.gt[b3];
+        __bf16* rm = which == 0 ? sm.qr[b3] : sm.gr[b3];
         bf16x8 y[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) y[u] = (vmask >> u) & 1 ? x[u] : bf16x8{};
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int row = 2 * rp + u;
-          *reinterpret_cast<bf16x8*>(&rm[row * DH + 8 * (c ^ row_swz<DH>(row))]) = y[u];
+          *reinterpret_cast<bf16x8*>(&rm[row * DH + 8 * (c ^ qsw<DH>(row))]) = y[u];
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          *reinterpret_cast<bf16x2*>(&tr[(8 * c + e) * kRp + ((2 * rp) ^ tsw(8 * c + e))]) =
-              bf16x2{y[0][e], y[1][e]};
       }
       if (tl < 32) {
         sm.lim[b2][tl] = mlim;
@@ -345,16 +367,16 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
           const int dg = NDH + i;
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            av[i] = mfma32(tr_frag<kRp>(sm.pt[b2], kw + nn, 16 * u, h),
-                           qt_frag(sm.gt[b3], 32 * dg + nn, 16 * u, h), av[i]);
-            ak[i] = mfma32(tr_frag<kRp>(sm.dst[b2], kw + nn, 16 * u, h),
-                           qt_frag(sm.qt[b3], 32 * dg + nn, 16 * u, h), ak[i]);
+            av[i] = mfma32(kt_frag(sm.pt[b2], kw + nn, 16 * u, h),
+                           qtr_frag<DH>(sm.gr[b3], 32 * dg, 16 * u, h, nn), av[i]);
+            ak[i] = mfma32(kt_frag(sm.dst[b2], kw + nn, 16 * u, h),
+                           qtr_frag<DH>(sm.qr[b3], 32 * dg, 16 * u, h, nn), ak[i]);
           }
         }
         if (kw < DH) {
 #pragma unroll
           for (int u = 0; u < 8; ++u)
-            acc = mfma32(fr[u], tr_frag<kDsp>(sm.ds[b2], nn, 16 * u, h), acc);
+            acc = mfma32(fr[u], ktr_frag(sm.dst[b2], 16 * u, h, nn), acc);
         }
       }
       const int R = 32 * T + n;
@@ -392,11 +414,11 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
         // they left a full LDS round trip in front of every MFMA: 128K
         // backward 46.1 -> 43.6 ms).
         f32x16 sa = {}, pa = {};
-        bf16x8 qa = rm_frag<DH>(sm.qr[b2], nn, 0, h), ga = rm_frag<DH>(sm.gr[b2], nn, 0, h);
+        bf16x8 qa = qr_frag<DH>(sm.qr[b3], nn, 0, h), ga = qr_frag<DH>(sm.gr[b3], nn, 0, h);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          const bf16x8 qn = s + 1 < S ? rm_frag<DH>(sm.qr[b2], nn, s + 1, h) : qa;
-          const bf16x8 gn = s + 1 < S ? rm_frag<DH>(sm.gr[b2], nn, s + 1, h) : ga;
+          const bf16x8 qn = s + 1 < S ? qr_frag<DH>(sm.qr[b3], nn, s + 1, h) : qa;
+          const bf16x8 gn = s + 1 < S ? qr_frag<DH>(sm.gr[b3], nn, s + 1, h) : ga;
           sa = mfma32(qa, fr[s], sa);
           pa = mfma32(ga, fr[S + s], pa);
           qa = qn;
@@ -420,23 +442,20 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
         for (int i = 0; i < NDH; ++i) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            av[i] = mfma32(pA[u], qt_frag(sm.gt[b3], 32 * i + nn, 16 * u, h), av[i]);
-            ak[i] = mfma32(dA[u], qt_frag(sm.qt[b3], 32 * i + nn, 16 * u, h), ak[i]);
+            av[i] = mfma32(pA[u], qtr_frag<DH>(sm.gr[b3], 32 * i, 16 * u, h, nn), av[i]);
+            ak[i] = mfma32(dA[u], qtr_frag<DH>(sm.qr[b3], 32 * i, 16 * u, h, nn), ak[i]);
           }
         }
-        // dS [row][key] for dQ; P^T and dS^T [key][row] for the consumers:
+        // P^T and dS^T [key][row] for the consumers (dS^T also feeds dQ):
         // registers 8u + 4q' .. +3 hold rows 16u + 8q' + 4h .. +3
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            sm.ds[b2][acc_row(8 * u + e, h) * kDsp + kw + nn] = dA[u][e];
-#pragma unroll
           for (int qh = 0; qh < 2; ++qh) {
             const int row0 = 16 * u + 8 * qh + 4 * h;
-            *reinterpret_cast<bf16x4*>(&sm.pt[b2][(kw + nn) * kRp + row0]) =
+            *reinterpret_cast<bf16x4*>(&sm.pt[b2][koff(kw + nn, row0)]) =
                 bf16x4{pA[u][4 * qh], pA[u][4 * qh + 1], pA[u][4 * qh + 2], pA[u][4 * qh + 3]};
-            *reinterpret_cast<bf16x4*>(&sm.dst[b2][(kw + nn) * kRp + row0]) =
+            *reinterpret_cast<bf16x4*>(&sm.dst[b2][koff(kw + nn, row0)]) =
                 bf16x4{dA[u][4 * qh], dA[u][4 * qh + 1], dA[u][4 * qh + 2], dA[u][4 * qh + 3]};
           }
         }
