@@ -35,6 +35,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kUnitRows = 16384;  // rows per work unit, at most
 constexpr int kUnitPos = 1024;    // positions per work unit, at most
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8) that wait for the vector memory counter alone.
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitVm0 = wait_vm(0);
+
 // The Q and dO rows of a 32-row tile sit row-major in LDS, their 16-byte
 // chunks XOR-swizzled by qsw(row).  Two kinds of read hit them: a fragment
 // read (16 lanes on 16 consecutive rows, one chunk each) and a transpose
@@ -194,27 +199,28 @@ __global__ __launch_bounds__(1024) void build_bwd_units_kernel(
 
 template <int DH>
 struct BwdSmem {
-  __bf16 qr[3][32 * DH];         // the tile's Q rows, row-major swizzled (three tiles live)
-  __bf16 gr[3][32 * DH];         // the tile's dO rows
+  __bf16 qr[4][32 * DH];         // the tile's Q rows, row-major swizzled (ring of four)
+  __bf16 gr[4][32 * DH];         // the tile's dO rows
   __bf16 pt[2][kBlock * 32];     // P^T [key][row], for the second d-half's dV
   __bf16 dst[2][kBlock * 32];    // dS^T [key][row], for its dK and for dQ
+  float ld[4][64];           // per tile row: lse, then D = dO . O
   int32_t lim[2][32];       // per tile row: last visible key of the block (-1: none)
-  float l2[2][32];          // lse * log2(e)
-  float dv[2][32];          // D = dO . O
   int32_t pos[kUnitPos];    // the unit's query positions
   uint8_t sl[kUnitPos];     // and the block's slot in each one's selection
 };
 
 // Eight waves per work-group, two per SIMD, in producer/consumer pairs
-// over the same 32 keys kw = 32 (w mod 4):
-//  - waves 0-3 (first d-half) form S = Q K^T and dP = dO V^T, the softmax
-//    and dS for tile T, add its P^T dO and dS^T Q into dV/dK for d < DH/2,
+// over the same 32 keys kw = 32 (w mod 4), each role in its own tile loop:
+//  - waves 0-3 fetch the row tiles (direct global -> LDS loads, two tiles
+//    ahead), form S = Q K^T and dP = dO V^T, the softmax and dS for tile T,
 //    and leave P^T and dS^T in LDS;
-//  - waves 4-7 take tile T-1 from LDS after the barrier: dV/dK for the
-//    second d-half, and dQ^T = K^T dS^T for their 32-wide d-slice (K^T in
-//    registers).
+//  - waves 4-7 take tile T-1 from LDS after the barrier: dV += P^T dO and
+//    dK += dS^T Q over all of d, and dQ^T = K^T dS^T for their 32-wide
+//    d-slice (K^T in registers).
 // No MFMA or softmax is done twice, and each SIMD holds one wave of each
-// kind, so one's softmax and LDS waits overlap the other's MFMAs.
+// kind, so one's softmax and LDS waits overlap the other's MFMAs.  The
+// producers do no transpose read: the compiler waits for every direct
+// load in flight before one, which would cut the prefetch to nothing.
 template <int DH>
 __global__ __launch_bounds__(512) void bwd_fused_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -295,130 +301,101 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
     // wait inside the loop has to cover them
     __builtin_amdgcn_s_waitcnt(0);
 
-    // tile staging: thread -> (tensor, 2-row group, 16-byte chunk)
-    const int which = tl / (16 * CH);  // 0: Q, 1: dO, 2+: none (wave-uniform)
-    const int it = tl % (16 * CH), rp = it / CH, c = it % CH;
     const int nrows = count * G;
     const int ntile = (nrows + 31) / 32;
     const int hq0 = r * G;
-    bf16x8 x[2];
-    int vmask = 0, mlim = -1;
-    float ml2 = 0.f, mdv = 0.f;
-    // Every thread issues the same global loads (idle staging threads and
-    // rows past the end read a valid row), so the compiler can count the
-    // loads and stores in flight instead of waiting for all of them.
-    auto load = [&](int T) {
-      vmask = 0;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int R = 32 * T + 2 * rp + u;
-        const bool ok = which < 2 && R < nrows;
-        const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
-        const int64_t pos = sm.pos[pp];
-        const int hq = hq0 + (ok ? R - pp * G : 0);
-        const __bf16* src = which == 0 ? Q + (pos * H_q + hq) * DH
-                                       : dO + ((pos - q_start) * H_q + hq) * DH;
-        x[u] = *reinterpret_cast<const bf16x8*>(src + 8 * c);
-        vmask |= (int)ok << u;
-      }
-      {
-        const int R = 32 * T + (tl & 31);
-        const bool ok = R < nrows;
-        const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
-        const int64_t pos = sm.pos[pp];
-        const int hq = hq0 + (ok ? R - pp * G : 0);
-        const int64_t ih = (pos - q_start) * H_q + hq;
-        ml2 = lse[ih];
-        mdv = D[ih];
-        mlim = ok ? (int)(pos - key0) : -1;
-      }
-    };
-    auto store = [&](int T) {
-      const int b2 = T & 1, b3 = T % 3;
-      if (which < 2) {
-        __bf16* rm = which == 0 ? sm.qr[b3] : sm.gr[b3];
-        bf16x8 y[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) y[u] = (vmask >> u) & 1 ? x[u] : bf16x8{};
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int row = 2 * rp + u;
-          *reinterpret_cast<bf16x8*>(&rm[row * DH + 8 * (c ^ qsw<DH>(row))]) = y[u];
-        }
-      }
-      if (tl < 32) {
-        sm.lim[b2][tl] = mlim;
-        sm.l2[b2][tl] = ml2 * kLog2e;
-        sm.dv[b2][tl] = mdv;
-      }
-    };
-    // consumer work on tile T (its producers' LDS output is complete): dV/dK
-    // of the second d-half, then dQ^T of the wave's d-slice stored as the
-    // rows' bf16 partials.  With T < 0 (nothing to consume) the MFMAs are
-    // skipped and zeros go to the spare slot, so the stores stay uniform.
-    f32x16 ak[NDH], av[NDH];
-    auto consume = [&](int T, int nn) {
-      const bool live = T >= 0;
-      const int b2 = T & 1, b3 = (T + 3) % 3;
-      f32x16 acc = {};
-      if (live) {
-#pragma unroll
-        for (int i = 0; i < NDH; ++i) {
-          const int dg = NDH + i;
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            av[i] = mfma32(kt_frag(sm.pt[b2], kw + nn, 16 * u, h),
-                           qtr_frag<DH>(sm.gr[b3], 32 * dg, 16 * u, h, nn), av[i]);
-            ak[i] = mfma32(kt_frag(sm.dst[b2], kw + nn, 16 * u, h),
-                           qtr_frag<DH>(sm.qr[b3], 32 * dg, 16 * u, h, nn), ak[i]);
-          }
-        }
-        if (kw < DH) {
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            acc = mfma32(fr[u], ktr_frag(sm.dst[b2], 16 * u, h, nn), acc);
-        }
-      }
-      const int R = 32 * T + n;
-      const bool ok = live && kw < DH && R < nrows;
+    // unit row R -> its position and query head (rows past the end take the
+    // unit's first row, so every load stays valid)
+    auto row_of = [&](int R, int64_t& pos, int& hq) {
+      const bool ok = R < nrows;
       const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
-      const int64_t ps = ok ? (sm.pos[pp] - q_start) * k + sm.sl[pp] : spare;
-      const int hl = ok ? R - pp * G : 0;
-      __bf16* dstp = part + (ps * H_kv + r) * (DH / 4) * G * 4 + hl * 4;
-      // accumulator rows are d = kw + 8qd + 4h + {0..3}: d-quad 8kq + 2qd + h
-      const int dq0 = ok ? 8 * kq : 0;
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-        *reinterpret_cast<bf16x4*>(dstp + (int64_t)(dq0 + 2 * qd + h) * G * 4) =
-            bf16x4{f2bf(acc[4 * qd]), f2bf(acc[4 * qd + 1]), f2bf(acc[4 * qd + 2]),
-                   f2bf(acc[4 * qd + 3])};
+      pos = sm.pos[pp];
+      hq = hq0 + (ok ? R - pp * G : 0);
     };
-
-    __syncthreads();  // positions staged
-    load(0);
-    store(0);
-    if (ntile > 1) load(1);
-    __syncthreads();
+    // Tile T's Q and dO rows go global -> LDS by direct loads (no registers),
+    // issued by the producer waves two tiles ahead into a ring of four: each
+    // wave-instruction fills one contiguous KiB, lane i writing bytes
+    // 16i..16i+15 (rows v*RPI.., chunk slot i % CH), and a lane fetches the
+    // global chunk that the swizzle keeps at its slot.  The tile's lse and D
+    // follow the same way, issued last by producer wave 0 (lane i < 32: lse
+    // of row i; lane 32 + i: D of row i).
+    constexpr int RPI = 1024 / (2 * DH);  // rows per wave-instruction
+    constexpr int NI = 32 / RPI;          // wave-instructions per tensor and tile
+    constexpr int PW = NI / 2;            // per producer wave (Q and dO together)
+    // the wave index in a scalar register: the LDS destination must be
+    // wave-uniform
+    const int kqs = __builtin_amdgcn_readfirstlane(kq);
+    auto dma = [&](int T) {
+      const int b4 = T & 3;
 #pragma unroll
-    for (int i = 0; i < NDH; ++i) ak[i] = av[i] = f32x16{};
-    for (int T = 0; T < ntile; ++T) {
-      const int b2 = T & 1, b3 = T % 3;
-      // LDS indices go through an opaque copy of n so that the fragment
-      // reads stay inside the loop rather than being hoisted into registers
-      int nn = n;
-      asm volatile("" : "+v"(nn));
-      if (dh == 0) {
-        // S = Q K^T and dP = dO V^T for the wave's 32 keys (key on the lane)
+      for (int u = 0; u < PW; ++u) {
+        const int v = kqs * PW + u, tens = v / NI, vi = v % NI;
+        const int row = vi * RPI + lane / CH, cs = lane % CH;
+        int64_t pos;
+        int hq;
+        row_of(32 * T + row, pos, hq);
+        const __bf16* src = (tens == 0 ? Q + (pos * H_q + hq) * DH
+                                       : dO + ((pos - q_start) * H_q + hq) * DH) +
+                            8 * (cs ^ qsw<DH>(row));
+        __builtin_amdgcn_global_load_lds(
+            static_cast<const void*>(src),
+            static_cast<void*>((tens == 0 ? sm.qr[b4] : sm.gr[b4]) + vi * RPI * DH), 16, 0, 0);
+      }
+      if (kqs == 0) {
+        int64_t pos;
+        int hq;
+        row_of(32 * T + (lane & 31), pos, hq);
+        const int64_t ih = (pos - q_start) * H_q + hq;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(lane < 32 ? lse + ih : D + ih),
+                                         static_cast<void*>(sm.ld[b4]), 4, 0, 0);
+      }
+    };
+    // last visible key of each row of tile T (wave 0, lanes 0..31)
+    auto put_lim = [&](int T) {
+      if (tl < 32) {
+        const int R = 32 * T + tl;
+        int64_t pos;
+        int hq;
+        row_of(R, pos, hq);
+        sm.lim[T & 1][tl] = R < nrows ? (int)(pos - key0) : -1;
+      }
+    };
+    // A producer wave's only memory-counter operations in the tile loop are
+    // these loads, so "all but its last loads (those of tile T+2) done"
+    // means tile T+1 has landed.
+    auto wait_tile = [&](bool more) {
+      if (!more)
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      else if (kqs == 0)
+        __builtin_amdgcn_s_waitcnt(wait_vm(PW + 1));
+      else
+        __builtin_amdgcn_s_waitcnt(wait_vm(PW));
+    };
+    __syncthreads();  // positions staged
+    if (dh == 0) {
+      // ---- producer waves: S, dP, softmax, dS; P^T and dS^T into LDS ----
+      dma(0);
+      if (ntile > 1) dma(1);
+      put_lim(0);
+      wait_tile(ntile > 1);
+      __syncthreads();
+      for (int T = 0; T < ntile; ++T) {
+        const int b2 = T & 1, b4 = T & 3;
+        // LDS indices go through an opaque copy of n so that the fragment
+        // reads stay inside the loop rather than being hoisted into registers
+        int nn = n;
+        asm volatile("" : "+v"(nn));
+        const bool more = T + 2 < ntile;
+        if (more) dma(T + 2);
+        // S = Q K^T and dP = dO V^T for the wave's 32 keys (key on the lane).
         // Each k-step's Q and dO fragments are read while the previous
-        // step's two MFMAs run (read one by one, each waited for at once,
-        // they left a full LDS round trip in front of every MFMA: 128K
-        // backward 46.1 -> 43.6 ms).
+        // step's two MFMAs run.
         f32x16 sa = {}, pa = {};
-        bf16x8 qa = qr_frag<DH>(sm.qr[b3], nn, 0, h), ga = qr_frag<DH>(sm.gr[b3], nn, 0, h);
+        bf16x8 qa = qr_frag<DH>(sm.qr[b4], nn, 0, h), ga = qr_frag<DH>(sm.gr[b4], nn, 0, h);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-          const bf16x8 qn = s + 1 < S ? qr_frag<DH>(sm.qr[b3], nn, s + 1, h) : qa;
-          const bf16x8 gn = s + 1 < S ? qr_frag<DH>(sm.gr[b3], nn, s + 1, h) : ga;
+          const bf16x8 qn = s + 1 < S ? qr_frag<DH>(sm.qr[b4], nn, s + 1, h) : qa;
+          const bf16x8 gn = s + 1 < S ? qr_frag<DH>(sm.gr[b4], nn, s + 1, h) : ga;
           sa = mfma32(qa, fr[s], sa);
           pa = mfma32(ga, fr[S + s], pa);
           qa = qn;
@@ -431,23 +408,14 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
           for (int e = 0; e < 8; ++e) {
             const int row = acc_row(8 * u + e, h);
             const int lm = sm.lim[b2][row];
-            const float l2 = sm.l2[b2][row], dv = sm.dv[b2][row];
+            const float l2 = sm.ld[b4][row] * kLog2e, dv = sm.ld[b4][32 + row];
             const float ex = __builtin_amdgcn_exp2f(sa[8 * u + e] * scale_log2 - l2);
             const float p = kw + n <= lm ? ex : 0.f;
             pA[u][e] = f2bf(p);
             dA[u][e] = f2bf(p * (pa[8 * u + e] - dv));
           }
-        // dV += P^T dO and dK += dS^T Q over the tile's rows, first d-half
-#pragma unroll
-        for (int i = 0; i < NDH; ++i) {
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            av[i] = mfma32(pA[u], qtr_frag<DH>(sm.gr[b3], 32 * i, 16 * u, h, nn), av[i]);
-            ak[i] = mfma32(dA[u], qtr_frag<DH>(sm.qr[b3], 32 * i, 16 * u, h, nn), ak[i]);
-          }
-        }
-        // P^T and dS^T [key][row] for the consumers (dS^T also feeds dQ):
-        // registers 8u + 4q' .. +3 hold rows 16u + 8q' + 4h .. +3
+        // P^T and dS^T [key][row] for the consumers: registers 8u + 4q' ..
+        // +3 hold rows 16u + 8q' + 4h .. +3
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
@@ -459,44 +427,85 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
                 bf16x4{dA[u][4 * qh], dA[u][4 * qh + 1], dA[u][4 * qh + 2], dA[u][4 * qh + 3]};
           }
         }
-        // producers store no dQ; the same (zero, spare-slot) stores as the
-        // consumers keep the memory counters uniform
-        consume(-1, nn);
-      } else {
-        consume(T - 1, nn);
+        if (T + 1 < ntile) put_lim(T + 1);
+        wait_tile(more);  // tile T+1 is in LDS
+        __syncthreads();
       }
-      (void)b3;
-      // the next tile's rows into the free buffers, then fetch the one after
-      if (T + 1 < ntile) {
-        store(T + 1);
-        if (T + 2 < ntile) load(T + 2);
-      }
-      __syncthreads();
-    }
-    if (dh == 1) consume(ntile - 1, n);
-    // the unit's dK/dV sums: accumulator rows are keys, the lane is d
-    if (pidx < 0) {
+    } else {
+      // ---- consumer waves, one tile behind: dV += P^T dO and dK += dS^T Q
+      // for all of d, and dQ^T = K^T dS^T for the wave's 32-wide d-slice,
+      // stored as the rows' bf16 partials ----
+      f32x16 ak[NDG], av[NDG];
 #pragma unroll
-      for (int i = 0; i < NDH; ++i)
+      for (int i = 0; i < NDG; ++i) ak[i] = av[i] = f32x16{};
+      auto consume = [&](int T, int nn) {
+        const int b2 = T & 1, b4 = T & 3;
+        bf16x8 pf[2], sf[2];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int64_t key = key0 + kw + acc_row(j, h);
-          if (key < Nk) {
-            const int64_t off = (key * H_kv + r) * DH + 32 * (NDH * dh + i) + n;
-            dK[off] += scale * ak[i][j];
-            dV[off] += av[i][j];
+        for (int u = 0; u < 2; ++u) {
+          pf[u] = kt_frag(sm.pt[b2], kw + nn, 16 * u, h);
+          sf[u] = kt_frag(sm.dst[b2], kw + nn, 16 * u, h);
+        }
+#pragma unroll
+        for (int dg = 0; dg < NDG; ++dg) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            av[dg] = mfma32(pf[u], qtr_frag<DH>(sm.gr[b4], 32 * dg, 16 * u, h, nn), av[dg]);
+            ak[dg] = mfma32(sf[u], qtr_frag<DH>(sm.qr[b4], 32 * dg, 16 * u, h, nn), ak[dg]);
           }
         }
-    } else {
-      float* pk = kvpart + (int64_t)pidx * 2 * kBlock * DH;
+        if (kw < DH) {
+          f32x16 acc = {};
 #pragma unroll
-      for (int i = 0; i < NDH; ++i)
+          for (int u = 0; u < 8; ++u) acc = mfma32(fr[u], ktr_frag(sm.dst[b2], 16 * u, h, nn), acc);
+          // rows past the end store zeros to the spare slot
+          const int R = 32 * T + n;
+          const bool ok = R < nrows;
+          const int pp = ok ? (int)__fmul_rn(__fadd_rn((float)R, 0.5f), inv_G) : 0;
+          const int64_t ps = ok ? (sm.pos[pp] - q_start) * k + sm.sl[pp] : spare;
+          const int hl = ok ? R - pp * G : 0;
+          __bf16* dstp = part + (ps * H_kv + r) * (DH / 4) * G * 4 + hl * 4;
+          // accumulator rows are d = kw + 8qd + 4h + {0..3}: d-quad 8kq + 2qd + h
+          const int dq0 = ok ? 8 * kq : 0;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int kr = kw + acc_row(j, h), d = 32 * (NDH * dh + i) + n;
-          pk[kr * DH + d] = ak[i][j];
-          pk[(kBlock + kr) * DH + d] = av[i][j];
+          for (int qd = 0; qd < 4; ++qd)
+            *reinterpret_cast<bf16x4*>(dstp + (int64_t)(dq0 + 2 * qd + h) * G * 4) =
+                bf16x4{f2bf(acc[4 * qd]), f2bf(acc[4 * qd + 1]), f2bf(acc[4 * qd + 2]),
+                       f2bf(acc[4 * qd + 3])};
         }
+      };
+      __syncthreads();  // the producers' first tile is staged
+      for (int T = 0; T < ntile; ++T) {
+        int nn = n;
+        asm volatile("" : "+v"(nn));
+        if (T > 0) consume(T - 1, nn);
+        __syncthreads();
+      }
+      consume(ntile - 1, n);
+      // the unit's dK/dV sums: accumulator rows are keys, the lane is d
+      if (pidx < 0) {
+#pragma unroll
+        for (int i = 0; i < NDG; ++i)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int64_t key = key0 + kw + acc_row(j, h);
+            if (key < Nk) {
+              const int64_t off = (key * H_kv + r) * DH + 32 * i + n;
+              dK[off] += scale * ak[i][j];
+              dV[off] += av[i][j];
+            }
+          }
+      } else {
+        float* pk = kvpart + (int64_t)pidx * 2 * kBlock * DH;
+#pragma unroll
+        for (int i = 0; i < NDG; ++i)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int kr = kw + acc_row(j, h), d = 32 * i + n;
+            pk[kr * DH + d] = ak[i][j];
+            pk[(kBlock + kr) * DH + d] = av[i][j];
+          }
+      }
     }
   }
 }
