@@ -11,13 +11,13 @@
 // One KV-outer pass over the forward's inverted index (local positions
 // included, with the causal mask).  A work unit is one bucket (group r,
 // block b), or a fixed-size slice of a large one.  Its work-group keeps
-// the block's K and V in registers (each 32-key slice on its own waves)
-// and sweeps the unit's rows -- (position, head) pairs -- in 32-row tiles
-// staged row-major in LDS: S = Q K^T and dP = dO V^T read them as plain
-// fragments, dV += P^T dO and dK += dS^T Q (the contractions over rows)
-// through the transpose read, so no transposed copy is made.  Each tile's
-// dS^T goes through LDS so that the waves, now owning 32 d each, form
-// dQ^T = K^T dS^T over all 128 keys; that is stored as a bf16
+// the block's K and V in registers and sweeps the unit's rows -- (position,
+// head) pairs -- in 32-row tiles staged row-major in LDS: S^T = K Q^T and
+// dP^T = V dO^T read them as plain fragments, dV += P^T dO and
+// dK += dS^T Q (the contractions over rows) through the transpose read, so
+// no transposed copy is made.  Each tile's P and dS go through LDS; dS
+// also feeds dQ^T = K^T dS^T over all 128 keys, formed by waves owning 32
+// d each and stored as a bf16
 // partial per (i, h, slot) and summed per (i, h) in ascending slot order by
 // a second kernel.  A whole bucket adds its dK/dV sums to the outputs at
 // the end; the slices of a split bucket write fp32 partials that a third
@@ -89,24 +89,26 @@ __device__ __forceinline__ bf16x8 qtr_frag(const __bf16* blk, int d0, int c0, in
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// P^T and dS^T tiles [key][32 rows]: 8-byte pieces (4 rows) XOR-swizzled
-// by key, so that 32 keys storing one piece each, 32 keys reading their
-// rows and a transpose read over 4 keys x 32 rows all hit distinct banks.
-__device__ __forceinline__ int koff(int key, int row) {
-  return key * 32 + 4 * ((row >> 2) ^ ((key >> 2) & 7)) + (row & 3);
+// P and dS tiles [32 rows][128 keys]: 8-byte pieces (4 keys) XOR-swizzled
+// by psw(row), which moves the row's low two bits to the piece index's top
+// bits.  Then 32 rows storing or reading one piece each, and a transpose
+// read over 4 rows x 32 keys, all land on distinct banks.
+__device__ __forceinline__ int poff(int row, int key) {
+  return row * kBlock + 4 * ((key >> 2) ^ (((row & 3) << 3) | ((row >> 2) & 7))) + (key & 3);
 }
-// Operand holding key `key` at tile rows c0 + 4h + {0..3}, c0 + 8 + 4h + {0..3}.
-__device__ __forceinline__ bf16x8 kt_frag(const __bf16* t, int key, int c0, int h) {
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&t[koff(key, c0 + 4 * h)]);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&t[koff(key, c0 + 8 + 4 * h)]);
+// Operand holding tile row `row` at keys c0 + 4h + {0..3}, c0 + 8 + 4h + {0..3}.
+__device__ __forceinline__ bf16x8 pr_frag(const __bf16* t, int row, int c0, int h) {
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(&t[poff(row, c0 + 4 * h)]);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(&t[poff(row, c0 + 8 + 4 * h)]);
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
-// Operand with the contraction over keys c0..c0+15: lane (n, h) gets tile
-// row n at keys c0 + 4h + {0..3} and c0 + 8 + 4h + {0..3} (transpose read).
-__device__ __forceinline__ bf16x8 ktr_frag(const __bf16* t, int c0, int h, int n) {
-  const int key = c0 + 4 * h + ((n >> 2) & 3), row = (n & 16) + 4 * (n & 3);
-  const bf16x4 lo = ld_tr(t + koff(key, row));
-  const bf16x4 hi = ld_tr(t + koff(key + 8, row));
+// Operand with the contraction over tile rows c0..c0+15: lane (n, h) gets
+// key k0 + n at rows c0 + 4h + {0..3} and c0 + 8 + 4h + {0..3} (transpose
+// read).
+__device__ __forceinline__ bf16x8 ptr_frag(const __bf16* t, int k0, int c0, int h, int n) {
+  const int row = c0 + 4 * h + ((n >> 2) & 3), key = k0 + (n & 16) + 4 * (n & 3);
+  const bf16x4 lo = ld_tr(t + poff(row, key));
+  const bf16x4 hi = ld_tr(t + poff(row + 8, key));
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -201,22 +203,24 @@ template <int DH>
 struct BwdSmem {
   __bf16 qr[4][32 * DH];         // the tile's Q rows, row-major swizzled (ring of four)
   __bf16 gr[4][32 * DH];         // the tile's dO rows
-  __bf16 pt[2][kBlock * 32];     // P^T [key][row], for the second d-half's dV
-  __bf16 dst[2][kBlock * 32];    // dS^T [key][row], for its dK and for dQ
+  __bf16 pb[2][32 * kBlock];     // P [row][key], for dV
+  __bf16 db[2][32 * kBlock];     // dS [row][key], for dK and dQ
   float ld[4][64];           // per tile row: lse, then D = dO . O
   int32_t lim[2][32];       // per tile row: last visible key of the block (-1: none)
   int32_t pos[kUnitPos];    // the unit's query positions
   uint8_t sl[kUnitPos];     // and the block's slot in each one's selection
 };
 
-// Eight waves per work-group, two per SIMD, in producer/consumer pairs
-// over the same 32 keys kw = 32 (w mod 4), each role in its own tile loop:
-//  - waves 0-3 fetch the row tiles (direct global -> LDS loads, two tiles
-//    ahead), form S = Q K^T and dP = dO V^T, the softmax and dS for tile T,
-//    and leave P^T and dS^T in LDS;
+// Eight waves per work-group, two per SIMD, producers and consumers, each
+// role in its own tile loop:
+//  - waves 0-3 (keys kw = 32w ..) fetch the row tiles (direct global -> LDS
+//    loads, two tiles ahead), form S^T = K Q^T and dP^T = V dO^T, the
+//    softmax and dS for tile T (the row on the lane), and leave P and dS
+//    in LDS;
 //  - waves 4-7 take tile T-1 from LDS after the barrier: dV += P^T dO and
-//    dK += dS^T Q over all of d, and dQ^T = K^T dS^T for their 32-wide
-//    d-slice (K^T in registers).
+//    dK += dS^T Q for a 64-key x 64-d quarter (d = 128; 32 keys x all of
+//    d for d = 64), and dQ^T = K^T dS^T for a 32-wide d-slice (K^T in
+//    registers).
 // No MFMA or softmax is done twice, and each SIMD holds one wave of each
 // kind, so one's softmax and LDS waits overlap the other's MFMAs.  The
 // producers do no transpose read: the compiler waits for every direct
@@ -373,7 +377,7 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
     };
     __syncthreads();  // positions staged
     if (dh == 0) {
-      // ---- producer waves: S, dP, softmax, dS; P^T and dS^T into LDS ----
+      // ---- producer waves: S^T, dP^T, softmax, dS; P and dS into LDS ----
       dma(0);
       if (ntile > 1) dma(1);
       put_lim(0);
@@ -387,43 +391,44 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
         asm volatile("" : "+v"(nn));
         const bool more = T + 2 < ntile;
         if (more) dma(T + 2);
-        // S = Q K^T and dP = dO V^T for the wave's 32 keys (key on the lane).
-        // Each k-step's Q and dO fragments are read while the previous
-        // step's two MFMAs run.
+        // S^T = K Q^T and dP^T = V dO^T for the wave's 32 keys: the row on
+        // the lane, keys in the registers, so each lane needs the row's lse,
+        // D and mask bound only.  Each k-step's Q and dO fragments are read
+        // while the previous step's two MFMAs run.
         f32x16 sa = {}, pa = {};
         bf16x8 qa = qr_frag<DH>(sm.qr[b4], nn, 0, h), ga = qr_frag<DH>(sm.gr[b4], nn, 0, h);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
           const bf16x8 qn = s + 1 < S ? qr_frag<DH>(sm.qr[b4], nn, s + 1, h) : qa;
           const bf16x8 gn = s + 1 < S ? qr_frag<DH>(sm.gr[b4], nn, s + 1, h) : ga;
-          sa = mfma32(qa, fr[s], sa);
-          pa = mfma32(ga, fr[S + s], pa);
+          sa = mfma32(fr[s], qa, sa);
+          pa = mfma32(fr[S + s], ga, pa);
           qa = qn;
           ga = gn;
         }
         bf16x8 pA[2], dA[2];
+        const int lm = sm.lim[b2][nn];
+        const float l2 = sm.ld[b4][nn] * kLog2e, dv = sm.ld[b4][32 + nn];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int row = acc_row(8 * u + e, h);
-            const int lm = sm.lim[b2][row];
-            const float l2 = sm.ld[b4][row] * kLog2e, dv = sm.ld[b4][32 + row];
+            const int key = kw + acc_row(8 * u + e, h);
             const float ex = __builtin_amdgcn_exp2f(sa[8 * u + e] * scale_log2 - l2);
-            const float p = kw + n <= lm ? ex : 0.f;
+            const float p = key <= lm ? ex : 0.f;
             pA[u][e] = f2bf(p);
             dA[u][e] = f2bf(p * (pa[8 * u + e] - dv));
           }
-        // P^T and dS^T [key][row] for the consumers: registers 8u + 4q' ..
-        // +3 hold rows 16u + 8q' + 4h .. +3
+        // P and dS [row][key] for the consumers: registers 8u + 4q' .. +3
+        // hold keys kw + 16u + 8q' + 4h .. +3
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
 #pragma unroll
           for (int qh = 0; qh < 2; ++qh) {
-            const int row0 = 16 * u + 8 * qh + 4 * h;
-            *reinterpret_cast<bf16x4*>(&sm.pt[b2][koff(kw + nn, row0)]) =
+            const int kc = kw + 16 * u + 8 * qh + 4 * h;
+            *reinterpret_cast<bf16x4*>(&sm.pb[b2][poff(nn, kc)]) =
                 bf16x4{pA[u][4 * qh], pA[u][4 * qh + 1], pA[u][4 * qh + 2], pA[u][4 * qh + 3]};
-            *reinterpret_cast<bf16x4*>(&sm.dst[b2][koff(kw + nn, row0)]) =
+            *reinterpret_cast<bf16x4*>(&sm.db[b2][poff(nn, kc)]) =
                 bf16x4{dA[u][4 * qh], dA[u][4 * qh + 1], dA[u][4 * qh + 2], dA[u][4 * qh + 3]};
           }
         }
@@ -433,31 +438,44 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
       }
     } else {
       // ---- consumer waves, one tile behind: dV += P^T dO and dK += dS^T Q
-      // for all of d, and dQ^T = K^T dS^T for the wave's 32-wide d-slice,
-      // stored as the rows' bf16 partials ----
-      f32x16 ak[NDG], av[NDG];
+      // for the wave's share of keys and d, and dQ^T = K^T dS^T for its
+      // 32-wide d-slice, stored as the rows' bf16 partials ----
+      // dV/dK split: the wave owns KG 32-key groups x DG 32-d groups (64 x 64
+      // for d = 128, so each operand fragment read feeds two MFMAs)
+      constexpr int KG = NDG >= 4 ? 2 : 1, DG = NDG / KG;
+      const int kb0 = 32 * KG * (kq / KG), db0 = 32 * DG * (kq % KG);
+      f32x16 ak[KG][DG], av[KG][DG];
 #pragma unroll
-      for (int i = 0; i < NDG; ++i) ak[i] = av[i] = f32x16{};
+      for (int a = 0; a < KG; ++a)
+#pragma unroll
+        for (int i = 0; i < DG; ++i) ak[a][i] = av[a][i] = f32x16{};
       auto consume = [&](int T, int nn) {
         const int b2 = T & 1, b4 = T & 3;
-        bf16x8 pf[2], sf[2];
+        bf16x8 pf[KG][2], sf[KG][2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          pf[u] = kt_frag(sm.pt[b2], kw + nn, 16 * u, h);
-          sf[u] = kt_frag(sm.dst[b2], kw + nn, 16 * u, h);
-        }
-#pragma unroll
-        for (int dg = 0; dg < NDG; ++dg) {
+        for (int a = 0; a < KG; ++a)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
-            av[dg] = mfma32(pf[u], qtr_frag<DH>(sm.gr[b4], 32 * dg, 16 * u, h, nn), av[dg]);
-            ak[dg] = mfma32(sf[u], qtr_frag<DH>(sm.qr[b4], 32 * dg, 16 * u, h, nn), ak[dg]);
+            pf[a][u] = ptr_frag(sm.pb[b2], kb0 + 32 * a, 16 * u, h, nn);
+            sf[a][u] = ptr_frag(sm.db[b2], kb0 + 32 * a, 16 * u, h, nn);
+          }
+#pragma unroll
+        for (int dg = 0; dg < DG; ++dg) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const bf16x8 gq = qtr_frag<DH>(sm.gr[b4], db0 + 32 * dg, 16 * u, h, nn);
+            const bf16x8 qq = qtr_frag<DH>(sm.qr[b4], db0 + 32 * dg, 16 * u, h, nn);
+#pragma unroll
+            for (int a = 0; a < KG; ++a) {
+              av[a][dg] = mfma32(pf[a][u], gq, av[a][dg]);
+              ak[a][dg] = mfma32(sf[a][u], qq, ak[a][dg]);
+            }
           }
         }
         if (kw < DH) {
           f32x16 acc = {};
 #pragma unroll
-          for (int u = 0; u < 8; ++u) acc = mfma32(fr[u], ktr_frag(sm.dst[b2], 16 * u, h, nn), acc);
+          for (int u = 0; u < 8; ++u) acc = mfma32(fr[u], pr_frag(sm.db[b2], nn, 16 * u, h), acc);
           // rows past the end store zeros to the spare slot
           const int R = 32 * T + n;
           const bool ok = R < nrows;
@@ -485,26 +503,30 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
       // the unit's dK/dV sums: accumulator rows are keys, the lane is d
       if (pidx < 0) {
 #pragma unroll
-        for (int i = 0; i < NDG; ++i)
+        for (int a = 0; a < KG; ++a)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int64_t key = key0 + kw + acc_row(j, h);
-            if (key < Nk) {
-              const int64_t off = (key * H_kv + r) * DH + 32 * i + n;
-              dK[off] += scale * ak[i][j];
-              dV[off] += av[i][j];
+          for (int i = 0; i < DG; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int64_t key = key0 + kb0 + 32 * a + acc_row(j, h);
+              if (key < Nk) {
+                const int64_t off = (key * H_kv + r) * DH + db0 + 32 * i + n;
+                dK[off] += scale * ak[a][i][j];
+                dV[off] += av[a][i][j];
+              }
             }
-          }
       } else {
         float* pk = kvpart + (int64_t)pidx * 2 * kBlock * DH;
 #pragma unroll
-        for (int i = 0; i < NDG; ++i)
+        for (int a = 0; a < KG; ++a)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int kr = kw + acc_row(j, h), d = 32 * i + n;
-            pk[kr * DH + d] = ak[i][j];
-            pk[(kBlock + kr) * DH + d] = av[i][j];
-          }
+          for (int i = 0; i < DG; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const int kr = kb0 + 32 * a + acc_row(j, h), d = db0 + 32 * i + n;
+              pk[kr * DH + d] = ak[a][i][j];
+              pk[(kBlock + kr) * DH + d] = av[a][i][j];
+            }
       }
     }
   }
