@@ -95,15 +95,28 @@ __device__ __forceinline__ void kl_item(const KlSmem<DH, DI>& sm, const __bf16* 
     // K fragments are read from LDS again for every head: an index the
     // compiler cannot see through keeps them from being hoisted out of the
     // head loop into registers.
+    // Each head's Q row and lse are requested one head ahead, so their
+    // latency hides under the previous head's MFMAs and exps (the last head
+    // requests its own row again).
+    auto ldq = [&](int hh, bf16x8* dst, float& l2o) {
+      const int hq = r * G + hh;
+      const __bf16* qrow = Q + ((int64_t)i * H_q + hq) * DH + (DH / 2) * h;
+#pragma unroll
+      for (int s = 0; s < S; ++s) dst[s] = *reinterpret_cast<const bf16x8*>(qrow + 8 * s);
+      l2o = lse[(int64_t)(i - (int)q_start) * H_q + hq];
+    };
+    bf16x8 qb[S];
+    float l2r;
+    ldq(0, qb, l2r);
     for (int hh = 0; hh < G; ++hh) {
       int nn = n;
       asm volatile("" : "+v"(nn));
-      const int hq = r * G + hh;
-      const __bf16* qrow = Q + ((int64_t)i * H_q + hq) * DH + (DH / 2) * h;
-      bf16x8 qb[S];
-#pragma unroll
-      for (int s = 0; s < S; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + 8 * s);
-      const float l2 = lse[(int64_t)(i - (int)q_start) * H_q + hq] * kLog2e;
+      bf16x8 qn[S];
+      float l2n;
+      ldq(min(hh + 1, G - 1), qn, l2n);
+      // the next head's loads stay ahead of this head's LDS reads and MFMAs
+      asm volatile("" ::: "memory");
+      const float l2 = l2r * kLog2e;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         f32x16 sacc = {};
@@ -113,6 +126,13 @@ __device__ __forceinline__ void kl_item(const KlSmem<DH, DI>& sm, const __bf16* 
         for (int j = 0; j < 16; ++j)
           t[g][j] += __builtin_amdgcn_exp2f(sacc[j] * scale_log2 - l2);
       }
+      // ... and land by the end of this head's work
+#pragma unroll
+      for (int s = 0; s < S; ++s) asm volatile("" : "+v"(qn[s]));
+      asm volatile("" : "+v"(l2n));
+#pragma unroll
+      for (int s = 0; s < S; ++s) qb[s] = qn[s];
+      l2r = l2n;
     }
     // student scores s = q_idx . k_idx over the block
     const __bf16* qirow = q_idx + ((int64_t)i * H_kv + r) * DI + (DI / 2) * h;
