@@ -112,6 +112,15 @@ __device__ __forceinline__ bf16x8 ptr_frag(const __bf16* t, int k0, int c0, int 
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Work-group barrier that waits for this wave's LDS operations only.  A
+// __syncthreads also waits for every direct global->LDS load in flight
+// (its fence covers their LDS writes); the producers instead wait for the
+// loads of the next tile alone, with an explicit counter wait, and leave
+// the tile after it in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace
 
 int bwd_unit_positions(int G) { return std::min(kUnitPos, std::max(1, kUnitRows / G)); }
@@ -382,7 +391,7 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
       if (ntile > 1) dma(1);
       put_lim(0);
       wait_tile(ntile > 1);
-      __syncthreads();
+      lds_barrier();
       for (int T = 0; T < ntile; ++T) {
         const int b2 = T & 1, b4 = T & 3;
         // LDS indices go through an opaque copy of n so that the fragment
@@ -434,7 +443,7 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
         }
         if (T + 1 < ntile) put_lim(T + 1);
         wait_tile(more);  // tile T+1 is in LDS
-        __syncthreads();
+        lds_barrier();
       }
     } else {
       // ---- consumer waves, one tile behind: dV += P^T dO and dK += dS^T Q
