@@ -13,12 +13,16 @@
 //       hist[tile][bucket] + lp[bucket] + (sum of agg before the bucket's
 //       work-group), and one wavefront walks the tile's queries in
 //       ascending order, appending each (query, slot) at its block's cursor.
-//       The tile-0 work-groups also write row_ptr.
+//       The tile-0 work-groups also write row_ptr.  Each XCD takes a
+//       contiguous range of tiles, so the short runs that neighbouring
+//       tiles append to one bucket are merged in one L2 (1M step: 1.97 ->
+//       1.65 ms).
 // Inside a bucket, positions therefore come out ascending.  Every global
 // read of a tile's selection rows is issued before the first use, so each
 // launch costs about one memory round trip per work-group.
 #include "common.h"
 #include "msa_internal.h"
+
 
 namespace msa {
 
@@ -93,13 +97,20 @@ __global__ __launch_bounds__(kScanWg) void csr_scan_kernel(int32_t* __restrict__
 __global__ __launch_bounds__(256) void csr_scatter_kernel(
     const int32_t* __restrict__ sel, int64_t q_start, int64_t Nq, int H_kv, int k, int nblk,
     const int32_t* __restrict__ hist, const int32_t* __restrict__ lp,
-    const int32_t* __restrict__ agg, int nwg, int32_t* __restrict__ row_ptr,
+    const int32_t* __restrict__ agg, int nwg, int ntiles, int32_t* __restrict__ row_ptr,
     int32_t* __restrict__ col, uint8_t* __restrict__ slot) {
   extern __shared__ int32_t smem[];
   int32_t* cur = smem;               // [nblk + 1]: the last one absorbs padding
   int32_t* aggp = cur + nblk + 1;    // [nwg + 1]
   int32_t* selt = aggp + nwg + 1;    // [kTile][k]
-  const int tile = blockIdx.x, r = blockIdx.y, t = threadIdx.x;
+  // work-group L runs on XCD L % 8; each XCD takes a contiguous range of
+  // tiles, so the runs that neighbouring tiles append to one bucket meet in
+  // that XCD's L2 instead of being written back from several
+  const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
+  const int tx = (ntiles + 7) >> 3;
+  const int r = j / tx, tile = xcd * tx + j % tx;
+  if (tile >= ntiles || r >= H_kv) return;
+  const int t = threadIdx.x;
   const int64_t iq0 = (int64_t)tile * kTile;
   const int nq = (int)min(Nq - iq0, (int64_t)kTile);
   const int n = nq * k;
@@ -222,8 +233,9 @@ hipError_t launch_invert(const int32_t* sel, int64_t q_start, int64_t Nq, int H_
   }
   csr_hist_kernel<<<dim3(ntiles, H_kv), 256, lds_hist, stream>>>(sel, Nq, H_kv, k, nblk, hist);
   csr_scan_kernel<<<(unsigned)nwg, kScanWg, 0, stream>>>(hist, ntiles, nb, lp, agg);
-  csr_scatter_kernel<<<dim3(ntiles, H_kv), 256, lds_scatter, stream>>>(
-      sel, q_start, Nq, H_kv, k, nblk, hist, lp, agg, nwg, row_ptr, col, slot);
+  const int tx = (ntiles + 7) / 8;
+  csr_scatter_kernel<<<(unsigned)(8 * tx * H_kv), 256, lds_scatter, stream>>>(
+      sel, q_start, Nq, H_kv, k, nblk, hist, lp, agg, nwg, ntiles, row_ptr, col, slot);
   return hipGetLastError();
 }
 
