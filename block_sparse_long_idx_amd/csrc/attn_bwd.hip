@@ -89,12 +89,22 @@ __device__ __forceinline__ bf16x8 qtr_frag(const __bf16* blk, int d0, int c0, in
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// P and dS tiles [32 rows][128 keys]: 8-byte pieces (4 keys) XOR-swizzled
-// by psw(row), which moves the row's low two bits to the piece index's top
-// bits.  Then 32 rows storing or reading one piece each, and a transpose
-// read over 4 rows x 32 keys, all land on distinct banks.
+// P and dS tiles [32 rows][128 keys] (256-byte rows): 8-byte pieces (4
+// keys) XOR-swizzled by psw(row).  Measured on gfx950, 8-byte LDS writes
+// are served 16 lanes at a time over 32 banks (the piece index mod 16
+// decides the banks) and reads 32 lanes at a time over 64 banks (mod 32).
+// psw puts the row's low two bits on the piece's top two bits and its
+// next two bits on the bottom two, with bit 1 of the row (flipped by bit
+// 4) in between, so that
+//  - 16 consecutive rows storing one piece differ mod 16 (producer stores),
+//  - 32 rows reading one piece differ mod 32 (the dQ operand reads),
+//  - a transpose read over 4 rows x 32 keys covers 32 distinct pieces.
+// (Without the middle bit, the stores took ~4 conflict cycles each.)
+__device__ __forceinline__ int psw(int row) {
+  return ((row & 3) << 3) | ((((row >> 1) ^ (row >> 4)) & 1) << 2) | ((row >> 2) & 3);
+}
 __device__ __forceinline__ int poff(int row, int key) {
-  return row * kBlock + 4 * ((key >> 2) ^ (((row & 3) << 3) | ((row >> 2) & 7))) + (key & 3);
+  return row * kBlock + 4 * ((key >> 2) ^ psw(row)) + (key & 3);
 }
 // Operand holding tile row `row` at keys c0 + 4h + {0..3}, c0 + 8 + 4h + {0..3}.
 __device__ __forceinline__ bf16x8 pr_frag(const __bf16* t, int row, int c0, int h) {
