@@ -428,6 +428,18 @@ __global__ __launch_bounds__(512) void bwd_fused_kernel(
         bf16x8 pA[2], dA[2];
         const int lm = sm.lim[b2][nn];
         const float l2 = sm.ld[b4][nn] * kLog2e, dv = sm.ld[b4][32 + nn];
+        // the causal mask only bites in tiles holding the block's own
+        // positions: elsewhere every row sees all of the wave's 32 keys
+        if (__builtin_amdgcn_ballot_w64(lm < kw + 31) == 0) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float p = __builtin_amdgcn_exp2f(sa[8 * u + e] * scale_log2 - l2);
+              pA[u][e] = f2bf(p);
+              dA[u][e] = f2bf(p * (pa[8 * u + e] - dv));
+            }
+        } else
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
