@@ -17,9 +17,8 @@
 // dK += dS^T Q (the contractions over rows) through the transpose read, so
 // no transposed copy is made.  Each tile's P and dS go through LDS; dS
 // also feeds dQ^T = K^T dS^T over all 128 keys, formed by waves owning 32
-// d each and stored as a bf16
-// partial per (i, h, slot) and summed per (i, h) in ascending slot order by
-// a second kernel.  A whole bucket adds its dK/dV sums to the outputs at
+// d each and stored as a bf16 partial per (i, h, slot), which a second
+// kernel sums per (i, h) in ascending slot order.  A whole bucket adds its dK/dV sums to the outputs at
 // the end; the slices of a split bucket write fp32 partials that a third
 // kernel sums in slice order.  Deterministic, no atomics on the outputs.
 #include "common.h"
