@@ -390,11 +390,22 @@ hipError_t launch_index_pool(const void* q_idx, const void* k_idx, int64_t q_sta
 //
 // Candidates are the blocks b < lb strictly before the local block.  Each
 // candidate becomes a unique 64-bit key (order-preserving score bits, then
-// ~b so that on equal scores the lower block ranks higher).  Every lane
-// scans a strided slice of the row and keeps its best LM keys in a sorted
-// register list; the wave then pops the global best k-1 keys one at a time
-// (a cross-lane max per pop, by DPP and ds_swizzle exchanges).  The local block is added and the k ids are
-// written in ascending order.
+// ~b so that on equal scores the lower block ranks higher); the k-1 largest
+// keys are selected, the local block is added and the k ids are written in
+// ascending order.
+//
+// A row of at most 128 candidates is held whole, two per lane.  A longer row
+// is read twice.  The first read takes each lane's best score over its
+// slice.  Those are scores of distinct blocks, so at least k-1 candidates
+// reach the (k-1)-th largest of them, tau, and no block scoring below tau
+// can be among the k-1 best.  The second read keeps the blocks
+// scoring at least tau, packed into LDS in the order the wave meets them
+// (a ballot and each lane's count of the set bits below it).  Few blocks
+// usually pass: up to 64 of them sit one per lane, and the wave pops the
+// best k-1 keys one at a time (a cross-lane max per pop, by DPP and
+// ds_swizzle exchanges).  When more pass (rows with many equal scores), a
+// third read lets every lane keep its best LM passing keys in a sorted
+// register list, and the pops take the heads of the lists.
 // ---------------------------------------------------------------------------
 template <int LM>
 __device__ __forceinline__ void list_insert(uint64_t (&lst)[LM], uint64_t key) {
@@ -406,42 +417,193 @@ __device__ __forceinline__ void list_insert(uint64_t (&lst)[LM], uint64_t key) {
   lst[0] = key > lst[0] ? key : lst[0];
 }
 
+__device__ __forceinline__ uint64_t block_key(float s, int b) {
+  return ((uint64_t)ord_f32(s) << 32) | (uint32_t)(~b);
+}
+
+// the score whose order key is o (the inverse of ord_f32)
+__device__ __forceinline__ float f32_of_ord(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// lanes below this one whose bit is set in the wave mask m
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// The maximum (MAX) or minimum over the 64 lanes, wave-uniform: DPP within
+// each 16-lane row, the four rows joined by readlane (no LDS traffic).
+template <bool MAX, int CTRL>
+__device__ __forceinline__ uint32_t dpp_pick_u32(uint32_t x) {
+  const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, 0xF, 0xF, false);
+  return MAX ? max(x, y) : min(x, y);
+}
+
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_pick_u32(uint32_t x) {
+  x = dpp_pick_u32<MAX, 0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x = dpp_pick_u32<MAX, 0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x = dpp_pick_u32<MAX, 0x141>(x);  // row_half_mirror
+  x = dpp_pick_u32<MAX, 0x140>(x);  // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+  return MAX ? max(max(a, b), max(c, d)) : min(min(a, b), min(c, d));
+}
+
+// The r-th largest (MAX) or smallest of the lanes' values, a value counted
+// once per lane that holds it; lanes holding `none` take no part, and
+// `none` is returned when fewer than r lanes do.  Each round takes the
+// cross-lane extreme and retires the lanes that hold it.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_rank_u32(uint32_t x, int r) {
+  constexpr uint32_t none = MAX ? 0u : 0xFFFFFFFFu;
+  for (;;) {
+    const uint32_t top = wave_pick_u32<MAX>(x);
+    const int held = __builtin_popcountll(__builtin_amdgcn_ballot_w64(x == top));
+    if (held >= r || top == none) return top;
+    r -= held;
+    if (x == top) x = none;
+  }
+}
+
+// A step reads kTopkLoads scores per lane, blocks b0 + 64u + lane, so that
+// all of a step's loads are in flight together.  Blocks at or past lb load
+// block lb - 1 (no branch around the load) and read as -inf.
+constexpr int kTopkLoads = 16;
+constexpr int kTopkStep = kWave * kTopkLoads;
+constexpr int kTopkPack = 2 * kWave;  // packed keys per wave, two per lane
+
+__device__ __forceinline__ void load_step(const float* __restrict__ prow, int b0, int lb,
+                                          int lane, float (&v)[kTopkLoads]) {
+#pragma unroll
+  for (int u = 0; u < kTopkLoads; ++u) {
+    const int b = b0 + kWave * u + lane;
+    const float x = prow[min(b, lb - 1)];
+    v[u] = b < lb ? x : -__builtin_inff();
+  }
+}
+
+// k1 pops of the cross-lane max over two sorted keys per lane (hd >= tl; 0
+// is below every key): lane p < k1 receives the p-th best block id.
+__device__ __forceinline__ void pop_pairs(uint64_t hd, uint64_t tl, int k1, int lane,
+                                          int& mine) {
+  for (int p = 0; p < k1; ++p) {
+    const uint64_t bk = wave_max_u64(hd);
+    if (hd == bk) {
+      hd = tl;
+      tl = 0;
+    }
+    if (lane == p) mine = (int)(~(uint32_t)bk);
+  }
+}
+
 template <int LM>
 __device__ __forceinline__ void topk_row(const float* __restrict__ prow, int lb, int k,
-                                         int32_t* __restrict__ out, int lane) {
+                                         int32_t* __restrict__ out, int lane,
+                                         uint64_t* __restrict__ cand) {
   const int K1 = k - 1;
   if (lb <= K1) {  // every visible block is selected
     if (lane < k) out[lane] = lane <= lb ? lane : -1;
     return;
   }
-  uint64_t lst[LM];
-#pragma unroll
-  for (int j = 0; j < LM; ++j) lst[j] = 0;  // below every real key
-  // Scores are read eight per lane at a time, so the loads of a batch are in
-  // flight together.
-  for (int b0 = 0; b0 < lb; b0 += 8 * kWave) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int b = b0 + kWave * u + lane;
-      v[u] = b < lb ? prow[b] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int b = b0 + kWave * u + lane;
-      const uint64_t key = ((uint64_t)ord_f32(v[u]) << 32) | (uint32_t)(~b);
-      if (b < lb && key > lst[LM - 1]) list_insert<LM>(lst, key);
-    }
-  }
   int mine = lb;  // lane K1 keeps the local block
-  for (int p = 0; p < K1; ++p) {
-    const uint64_t best = wave_max_u64(lst[0]);
-    if (lst[0] == best) {
+  if (K1 > 0 && lb <= 2 * kWave) {
+    // Short row: every block is a candidate, blocks lane and lane + 64.
+    const int b2 = lane + kWave;
+    uint64_t hd = lane < lb ? block_key(prow[lane], lane) : 0;
+    uint64_t tl = b2 < lb ? block_key(prow[min(b2, lb - 1)], b2) : 0;
+    pop_pairs(tl > hd ? tl : hd, tl > hd ? hd : tl, K1, lane, mine);
+  } else if (K1 > 0) {
+    // One read.  Every lane owns a block of the first step (lb > 128).
+    float best = -__builtin_inff();  // the lane's best score so far
+    int n = 0;  // keys packed so far, the same in every lane
+    uint32_t to = 0;  // order key of tau
+    float tau = -__builtin_inff();
+    for (int b0 = 0; b0 < lb; b0 += kTopkStep) {
+      float v[kTopkLoads];
+      load_step(prow, b0, lb, lane, v);
 #pragma unroll
-      for (int j = 0; j < LM - 1; ++j) lst[j] = lst[j + 1];
-      lst[LM - 1] = 0;
+      for (int u = 0; u < kTopkLoads; ++u) best = fmaxf(best, v[u]);
+      // fmaxf returns one of its operands, so each lane's best is the score
+      // of one of its blocks, and tau, the K1-th largest lane best, is
+      // reached by at least K1 blocks.  Usually only the lanes at or above
+      // the previous tau can hold it: with c of them (K1 <= c < 2 K1) it is
+      // their (c - K1 + 1)-th smallest, a few rounds from below.
+      const uint32_t bo = ord_f32(best);
+      const int c = b0 ? __builtin_popcountll(__builtin_amdgcn_ballot_w64(bo >= to)) : 0;
+      if (c >= K1 && c < 2 * K1)
+        to = wave_rank_u32<false>(bo >= to ? bo : 0xFFFFFFFFu, c - K1 + 1);
+      else
+        to = wave_rank_u32<true>(bo, K1);
+      tau = to ? f32_of_ord(to) : -__builtin_inff();
+      if (n > kTopkPack / 2 && n <= kTopkPack) {
+        // drop the packed keys that fell below tau
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint64_t c0 = lane < n ? cand[lane] : 0;
+        const uint64_t c1 = lane + kWave < n ? cand[lane + kWave] : 0;
+        const bool k0 = c0 && f32_of_ord((uint32_t)(c0 >> 32)) >= tau;
+        const bool k1 = c1 && f32_of_ord((uint32_t)(c1 >> 32)) >= tau;
+        const uint64_t m0 = __builtin_amdgcn_ballot_w64(k0);
+        const uint64_t m1 = __builtin_amdgcn_ballot_w64(k1);
+        const int n0 = __builtin_popcountll(m0);
+        if (k0) cand[lanes_below(m0)] = c0;
+        if (k1) cand[n0 + lanes_below(m1)] = c1;
+        n = n0 + __builtin_popcountll(m1);
+      }
+      // pack this step's blocks scoring >= tau, in the order the wave meets
+      // them; a count past kTopkPack marks the pack as overflowed
+#pragma unroll
+      for (int u = 0; u < kTopkLoads; ++u) {
+        const int b = b0 + kWave * u + lane;
+        const bool pass = b < lb && v[u] >= tau;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(pass);
+        if (m) {
+          const int pos = n + lanes_below(m);
+          if (pass && pos < kTopkPack) cand[pos] = block_key(v[u], b);
+          n += __builtin_popcountll(m);
+        }
+      }
     }
-    if (lane == p) mine = (int)(~(uint32_t)best);
+    // The wave's LDS accesses complete in order; the fences keep the
+    // compiler from moving the reads above the writes.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (n <= kTopkPack) {
+      const uint64_t c0 = lane < n ? cand[lane] : 0;
+      const uint64_t c1 = lane + kWave < n ? cand[lane + kWave] : 0;
+      pop_pairs(c1 > c0 ? c1 : c0, c1 > c0 ? c0 : c1, K1, lane, mine);
+    } else {
+      // the pack overflowed: read the row again, each lane keeping its best
+      // LM keys among the blocks scoring >= the final tau
+      uint64_t lst[LM];
+#pragma unroll
+      for (int j = 0; j < LM; ++j) lst[j] = 0;
+      for (int b0 = 0; b0 < lb; b0 += kTopkStep) {
+        float v[kTopkLoads];
+        load_step(prow, b0, lb, lane, v);
+#pragma unroll
+        for (int u = 0; u < kTopkLoads; ++u) {
+          const int b = b0 + kWave * u + lane;
+          const uint64_t key = block_key(v[u], b);
+          if (b < lb && v[u] >= tau && key > lst[LM - 1]) list_insert<LM>(lst, key);
+        }
+      }
+      for (int p = 0; p < K1; ++p) {
+        const uint64_t bk = wave_max_u64(lst[0]);
+        if (lst[0] == bk) {
+#pragma unroll
+          for (int j = 0; j < LM - 1; ++j) lst[j] = lst[j + 1];
+          lst[LM - 1] = 0;
+        }
+        if (lane == p) mine = (int)(~(uint32_t)bk);
+      }
+    }
   }
   // ascending order: rank of each of the k ids among lanes 0..k-1
   int rank = 0;
@@ -459,6 +621,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ P, 
                                                    int64_t nrows, int64_t Nq, int H_kv,
                                                    int64_t q_start, int nblk_dec, int k,
                                                    int32_t* __restrict__ sel) {
+  __shared__ uint64_t cand[4][kTopkPack];
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= nrows) return;
@@ -473,7 +636,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ P, 
     lb = (int)((q_start + iq) / kBlock);
     out = sel + (iq * H_kv + r) * k;
   }
-  topk_row<LM>(P + row * ldp, lb, k, out, lane);
+  topk_row<LM>(P + row * ldp, lb, k, out, lane, cand[threadIdx.x >> 6]);
 }
 
 static hipError_t launch_topk(const float* P, int64_t ldp, int64_t nrows, int64_t Nq,

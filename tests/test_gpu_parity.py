@@ -110,6 +110,54 @@ def test_index_topk_wide_tiles(oracle_lib, case):
     np.testing.assert_array_equal(sel.cpu().numpy(), ref)
 
 
+# Rows of more than 128 visible blocks, the two-kernel Top-k's thresholded
+# path (shorter rows are ranked whole).  "tiled" makes every key block a copy
+# of the first, so all of a query's blocks score alike, apart from blocks
+# whose keys are doubled (they outscore the rest wherever a query's best key
+# scores above zero).  More than 128 blocks then share the (k-1)-th best
+# score, the LDS pack overflows and the register-list path runs; ties go to
+# the lower block index.
+TOPK_LONG_CASES = [
+    # N, H_kv, d_idx, k, tiled, doubled blocks, q_start
+    (20000, 2, 64, 16, False, (), 17000),
+    (20000, 1, 32, 16, True, (), 18500),
+    (20000, 2, 64, 32, True, (), 19000),
+    (20000, 2, 32, 8, True, (5, 40, 77), 18000),
+]
+
+
+@pytest.mark.parametrize("case", TOPK_LONG_CASES,
+                         ids=lambda c: "N%d_Hkv%d_di%d_k%d_tiled%d_hot%d" % (c[:5] + (len(c[5]),)))
+def test_index_topk_long_rows(oracle_lib, case):
+    N, H_kv, d_idx, k, tiled, hot, q_start = case
+    say("index_topk long rows", case)
+    t = make_prefill_inputs(N, H_kv, H_kv, 64, d_idx, seed=N + 7 * k)
+    ki = t["k_idx"]
+    if tiled:
+        ki = ki[:128].repeat((N + 127) // 128, 1, 1)[:N].contiguous()
+    for b in hot:
+        ki[b * 128:(b + 1) * 128] *= 2
+    qi = t["q_idx"]
+    rows = np.arange(q_start, N)
+    uq, uk = bf16_bits(qi), bf16_bits(ki)
+    ref = oracle_lib.select(uq[rows], uk, rows, k)
+    if tiled:
+        # the case reaches the overflow path: the last row has more than 128
+        # blocks scoring at least its (k-1)-th best
+        i = N - 1
+        P = oracle_lib.block_scores(uq[i], uk, i, 0)[:i // 128]
+        assert (P >= np.sort(P)[::-1][k - 2]).sum() > 128
+    old = msa.get_option(msa.OPT_INDEX_FUSED)
+    try:
+        for fused in (0, 1):
+            msa.set_option(msa.OPT_INDEX_FUSED, fused)
+            sel = msa.index_topk(qi.cuda(), ki.cuda(), k, q_start=q_start, Nq=N - q_start)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(sel.cpu().numpy(), ref, err_msg=f"fused={fused}")
+    finally:
+        msa.set_option(msa.OPT_INDEX_FUSED, old)
+
+
 @pytest.mark.parametrize("case", STAGE_CASES, ids=lambda c: "N%d_k%d_qs%d" % (c[0], c[5], c[7]))
 def test_invert_stage(oracle_lib, case):
     N, H_q, H_kv, d_h, d_idx, k, n_hot, q_start, Nq = case
