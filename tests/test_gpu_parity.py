@@ -287,6 +287,34 @@ def test_decode(oracle_lib, case):
         assert_attn_close(O[b], O_ref, lse[b], l_ref)
 
 
+# Decode over more than 128 blocks with every key block a copy of the first
+# (all blocks score alike for each sequence), apart from sequence 1, whose
+# blocks 7 and 150 have their keys doubled: the Top-k's threshold passes
+# more than 128 blocks and its register-list path picks the lowest ids (and
+# the doubled blocks first where the best key scores above zero).
+def test_decode_ties(oracle_lib):
+    B, N, H_q, H_kv, d_h, d_idx, k = 2, 20000, 16, 2, 128, 64, 16
+    say("decode ties", (B, N, H_q, H_kv, d_h, d_idx, k))
+    t = make_decode_inputs(B, N, H_q, H_kv, d_h, d_idx, seed=77)
+    nb = (N + 127) // 128
+    t["k_idx"] = t["k_idx"][:, :128].repeat(1, nb, 1, 1)[:, :N].contiguous()
+    for blk in (7, 150):
+        t["k_idx"][1, blk * 128:(blk + 1) * 128] *= 2
+    scale = 1.0 / math.sqrt(d_h)
+    d = _dev(t)
+    sel, O, lse = msa.decode(d["q"], d["q_idx"], d["K"], d["V"], d["k_idx"], k, scale=scale)
+    torch.cuda.synchronize()
+    sel, O, lse = sel.cpu().numpy(), O.cpu().numpy(), lse.cpu().numpy()
+    for b in range(B):
+        u = {n: bf16_bits(t[n][b]) for n in t}
+        s_ref, O_ref, l_ref = oracle_lib.decode_one(u["q"], u["q_idx"], u["K"], u["V"],
+                                                    u["k_idx"], k, scale)
+        if b == 0:
+            assert (s_ref[:, :k - 1] == np.arange(k - 1)).all()  # all tied: lowest ids
+        np.testing.assert_array_equal(sel[b], s_ref)
+        assert_attn_close(O[b], O_ref, lse[b], l_ref)
+
+
 # ------------------------------------------------------ full-size workloads
 # Oracle results of the full-size workloads, shared by the two Index Branch
 # variants (the inputs are seeded, so both runs see the same tensors).
