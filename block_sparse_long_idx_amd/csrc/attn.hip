@@ -468,8 +468,8 @@ __global__ __launch_bounds__(256, 2) void combine_local_kernel(
   constexpr int NDG = DH / 32;
   extern __shared__ __attribute__((aligned(16))) char smem_raw[];
   AttnSmem<DH>& sm = *reinterpret_cast<AttnSmem<DH>*>(smem_raw);
-  const int r = blockIdx.y;
-  const int64_t b = q_start / kBlock + blockIdx.x;
+  const int r = blockIdx.x;
+  const int64_t b = q_start / kBlock + blockIdx.y;
   const int64_t p0 = max(q_start, b * kBlock), p1 = min(q_start + Nq, (b + 1) * kBlock);
   const int npos = (int)(p1 - p0);
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
@@ -699,7 +699,10 @@ hipError_t launch_combine(const void* Q, const void* K, const void* V, const voi
   const float inv_G = 1.f / (float)G;
   const float scale_log2 = scale * 1.4426950408889634f;
   const int64_t nqb = (q_start + Nq - 1) / kBlock - q_start / kBlock + 1;
-  dim3 grid((unsigned)nqb, H_kv), block(256);
+  // group fastest: the H_kv work-groups of a query block run together and
+  // read each (position, slot) partial record, all groups side by side,
+  // at once (0.5 % faster per 1M step than query blocks fastest)
+  dim3 grid((unsigned)H_kv, (unsigned)nqb), block(256);
   auto* q = static_cast<const __bf16*>(Q);
   auto* kk = static_cast<const __bf16*>(K);
   auto* v = static_cast<const __bf16*>(V);
