@@ -395,17 +395,19 @@ hipError_t launch_index_pool(const void* q_idx, const void* k_idx, int64_t q_sta
 // ascending order.
 //
 // A row of at most 128 candidates is held whole, two per lane.  A longer row
-// is read twice.  The first read takes each lane's best score over its
-// slice.  Those are scores of distinct blocks, so at least k-1 candidates
-// reach the (k-1)-th largest of them, tau, and no block scoring below tau
-// can be among the k-1 best.  The second read keeps the blocks
-// scoring at least tau, packed into LDS in the order the wave meets them
-// (a ballot and each lane's count of the set bits below it).  Few blocks
-// usually pass: up to 64 of them sit one per lane, and the wave pops the
-// best k-1 keys one at a time (a cross-lane max per pop, by DPP and
-// ds_swizzle exchanges).  When more pass (rows with many equal scores), a
-// third read lets every lane keep its best LM passing keys in a sorted
-// register list, and the pops take the heads of the lists.
+// is read once, in steps of 1,024 blocks.  After each step every lane's
+// best score so far is the score of one of its blocks, so at least k-1
+// candidates reach the (k-1)-th largest of those 64 bests, tau, and no block
+// scoring below tau can be among the k-1 best.  The step's blocks scoring
+// at least tau are packed into LDS in the order the wave meets them (a
+// ballot and each lane's count of the set bits below it); once the pack is
+// more than half full, the keys that fell below a risen tau are dropped
+// before the next step packs.  Few blocks usually pass: up to 128 of them
+// sit two per lane at the end, and the wave pops the best k-1 keys one at a
+// time (a cross-lane max per pop, by DPP and ds_swizzle exchanges).  When
+// more pass (rows with many equal scores), a second read lets every lane
+// keep its best LM keys scoring at least the final tau in a sorted register
+// list, and the pops take the heads of the lists.
 // ---------------------------------------------------------------------------
 template <int LM>
 __device__ __forceinline__ void list_insert(uint64_t (&lst)[LM], uint64_t key) {
