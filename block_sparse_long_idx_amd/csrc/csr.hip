@@ -103,6 +103,7 @@ __global__ __launch_bounds__(256) void csr_scatter_kernel(
   int32_t* cur = smem;               // [nblk + 1]: the last one absorbs padding
   int32_t* aggp = cur + nblk + 1;    // [nwg + 1]
   int32_t* selt = aggp + nwg + 1;    // [kTile][k]
+  int32_t* posq = selt + kTile * k;  // [8][32]: a walk step's positions
   // work-group L runs on XCD L % 8; each XCD takes a contiguous range of
   // tiles, so the runs that neighbouring tiles append to one bucket meet in
   // that XCD's L2 instead of being written back from several
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(256) void csr_scatter_kernel(
   }
   if (tile == 0 && r == H_kv - 1 && t == 0) row_ptr[(int64_t)H_kv * nblk] = aggp[nwg];
   __syncthreads();
-  if (t >= k) return;
+  if (t >= kWave) return;
   // Lanes 0..k-1 of the first wavefront walk the tile's queries in order;
   // lane s takes slot s (the k blocks of one query are distinct, so the
   // lanes of one instruction never share a cursor).  Each query's cursor
@@ -184,21 +185,39 @@ __global__ __launch_bounds__(256) void csr_scatter_kernel(
   // wavefront's instructions in issue order, so eight queries' updates go
   // out back to back and still take their positions in query order.
   // Padding entries (-1) and rows past the tile add to the spare cursor
-  // cur[nblk], so no atomic sits behind a branch.
+  // cur[nblk], so no atomic is behind a branch.  The eight queries'
+  // positions then pass through LDS so that every lane of the wave stores:
+  // a store instruction covers 64 / KS queries (KS = k rounded up to 16 or
+  // 32 lanes) instead of one, which keeps fewer stores in flight per entry.
+  const int KS = k <= 16 ? 16 : 32, QS = kWave / KS;
+  const int g = t / KS, sl = t % KS;
   if (t == 0) cur[nblk] = 0;
   for (int iq = 0; iq < nq; iq += 8) {
-    int32_t b[8], pos[8];
+    if (t < k) {
+      int32_t bb[8], pos[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) b[u] = iq + u < nq ? selt[(iq + u) * k + t] : -1;
+      for (int u = 0; u < 8; ++u) bb[u] = iq + u < nq ? selt[(iq + u) * k + t] : -1;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) pos[u] = atomicAdd(&cur[b[u] >= 0 ? b[u] : nblk], 1);
+      for (int u = 0; u < 8; ++u) pos[u] = atomicAdd(&cur[bb[u] >= 0 ? bb[u] : nblk], 1);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (b[u] >= 0) {
-        col[pos[u]] = (int32_t)(q_start + iq0 + iq + u);
-        slot[pos[u]] = (uint8_t)t;
+      for (int u = 0; u < 8; ++u) posq[u * KS + t] = bb[u] >= 0 ? pos[u] : -1;
+    }
+    // the wave's LDS accesses complete in order; the fences keep the
+    // compiler from moving the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int j = 0; j < 8; j += QS) {
+      const int qq = j + g;
+      const int32_t p = sl < k ? posq[qq * KS + sl] : -1;
+      if (p >= 0) {
+        col[p] = (int32_t)(q_start + iq0 + iq + qq);
+        slot[p] = (uint8_t)sl;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -219,13 +238,14 @@ hipError_t launch_invert(const int32_t* sel, int64_t q_start, int64_t Nq, int H_
   int32_t* hist = static_cast<int32_t*>(scratch);
   int32_t* lp = hist + (int64_t)ntiles * nb;
   int32_t* agg = lp + nb;
-  // scatter LDS: nblk + 1 + nwg + 1 + kTile * k ints, at most 16385 + 4097
-  // + 16384 (H_kv <= 64, nblk <= 16384, k <= 32): 144 KiB
+  // scatter LDS: nblk + 1 + nwg + 1 + kTile * k + 256 ints, at most 16385 +
+  // 4097 + 16384 + 256 (H_kv <= 64, nblk <= 16384, k <= 32): 145 KiB
   const size_t lds_hist = sizeof(int32_t) * (size_t)nblk;
-  const size_t lds_scatter = sizeof(int32_t) * ((size_t)nblk + 1 + nwg + 1 + (size_t)kTile * k);
+  const size_t lds_scatter =
+      sizeof(int32_t) * ((size_t)nblk + 1 + nwg + 1 + (size_t)kTile * k + 8 * 32);
   static bool lds_ready = false;
   if (!lds_ready) {
-    const int most = (int)(sizeof(int32_t) * (16385 + 4097 + kTile * 32));
+    const int most = (int)(sizeof(int32_t) * (16385 + 4097 + kTile * 32 + 8 * 32));
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&csr_scatter_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, most);
     if (e != hipSuccess) return e;
