@@ -62,12 +62,14 @@ struct RowStage {
 };
 
 // MFMA A fragment (32 keys x 16 d) of key group g, k-step s from a swizzled
-// block; lane half h covers d in [h*D/2, (h+1)*D/2) (the same permutation is
-// applied to the query operand, so the dot products are unchanged).
+// block; at k-step s lane half h covers d = 16s + 8h .. 16s + 8h + 7.  The
+// query operands take the same order, so the two lanes of a row read
+// neighbouring 16-byte pieces and each load instruction touches half as
+// many cache lines as with a contiguous half-row per lane.
 template <int D>
 __device__ __forceinline__ bf16x8 row_frag(const __bf16* blk, int g, int s, int h, int n) {
   const int row = 32 * g + n;
-  return *reinterpret_cast<const bf16x8*>(&blk[row * D + 8 * (((D / 16) * h + s) ^ row_swz<D>(row))]);
+  return *reinterpret_cast<const bf16x8*>(&blk[row * D + 8 * ((2 * s + h) ^ row_swz<D>(row))]);
 }
 
 // One work item: 32-position tiles, positions on the MFMA columns (S^T =
@@ -100,9 +102,9 @@ __device__ __forceinline__ void kl_item(const KlSmem<DH, DI>& sm, const __bf16* 
     // requests its own row again).
     auto ldq = [&](int hh, bf16x8* dst, float& l2o) {
       const int hq = r * G + hh;
-      const __bf16* qrow = Q + ((int64_t)i * H_q + hq) * DH + (DH / 2) * h;
+      const __bf16* qrow = Q + ((int64_t)i * H_q + hq) * DH + 8 * h;
 #pragma unroll
-      for (int s = 0; s < S; ++s) dst[s] = *reinterpret_cast<const bf16x8*>(qrow + 8 * s);
+      for (int s = 0; s < S; ++s) dst[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
       l2o = lse[(int64_t)(i - (int)q_start) * H_q + hq];
     };
     bf16x8 qb[S];
@@ -135,10 +137,10 @@ __device__ __forceinline__ void kl_item(const KlSmem<DH, DI>& sm, const __bf16* 
       l2r = l2n;
     }
     // student scores s = q_idx . k_idx over the block
-    const __bf16* qirow = q_idx + ((int64_t)i * H_kv + r) * DI + (DI / 2) * h;
+    const __bf16* qirow = q_idx + ((int64_t)i * H_kv + r) * DI + 8 * h;
     bf16x8 qi[SI];
 #pragma unroll
-    for (int s = 0; s < SI; ++s) qi[s] = *reinterpret_cast<const bf16x8*>(qirow + 8 * s);
+    for (int s = 0; s < SI; ++s) qi[s] = *reinterpret_cast<const bf16x8*>(qirow + 16 * s);
     f32x16 sc[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
